@@ -1,0 +1,347 @@
+"""Plain, slow, fp64 CPU oracle of the AXELRAM write and read paths.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test suite, the smoke check and the CPU-baseline
+leg of the benchmark use it.  It shares no code, tables or constants with the
+HIP library; it receives the same seeded inputs and nothing else.
+
+Source: "AXELRAM: Quantize Once, Never Dequantize" (arXiv 2604.02638),
+Abstract.  The abstract fixes: an orthogonal transform on write that makes each
+coordinate of a (unit) key approximately N(0, 1/d); a design-time codebook that
+is the optimal scalar quantizer for that density and depends only on (d, b); a
+table lookup on read with no inverse transform; and a seeded sign pattern.
+Where the abstract is silent this module takes the plainest reading:
+
+* the key is normalised to unit length and its Euclidean norm is stored
+  (otherwise a per-coordinate N(0, 1/d) law cannot hold for arbitrary keys);
+* the orthogonal transform is  y = H_d (s * x) / sqrt(d)  with s in {+1,-1}^d
+  the sign pattern and H_d the Sylvester-ordered Walsh-Hadamard matrix
+  H_d[i, j] = (-1)^popcount(i & j), signs applied first;
+* the optimal quantizer is the Lloyd-Max quantizer (centroid + midpoint
+  conditions) for N(0, 1/d); the Code-with-Papers record of the paper's
+  repository lists a Lloyd-Max solver next to a target-pdf and a
+  conditional-mean routine, which is the construction used here;
+* index of a coordinate = number of thresholds strictly below it (a value
+  equal to a threshold takes the lower cell);
+* the read-path table for query q is LUT[j][c] = q'_j * c_c with
+  q' = H_d (s * q) / sqrt(d) (queries are not normalised) and the score of
+  key k is ||k|| * sum_j LUT[j][idx_j];
+* a query head h reads KV head h // G where G = Hq / Hkv;
+* the b-bit indices of one key are stored as a little-endian bit stream:
+  bit r of idx_j is bit (j*b + r) of the key's record, record bit m is bit
+  m % 32 of 32-bit word m // 32.
+
+Every routine below is the definition written out with numpy in float64: the
+Hadamard transform is the dense matrix product (no butterflies), the quantizer
+is a comparison count, the score is a gather and a sum.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "gaussian_cell_mass",
+    "gaussian_cell_mean",
+    "lloyd_max_codebook",
+    "codebook_distortion",
+    "sylvester_hadamard",
+    "signs_from_bits",
+    "key_norms",
+    "rotate",
+    "transform_keys",
+    "transform_queries",
+    "quantize",
+    "pack_indices",
+    "unpack_indices",
+    "build_lut",
+    "lut_scores",
+    "score_condition",
+    "write_path",
+    "read_path",
+    "dequantize_then_dot",
+    "multiplications_per_query",
+]
+
+_SQRT2 = math.sqrt(2.0)
+
+
+# ---------------------------------------------------------------------------
+# Design-time codebook: Lloyd-Max quantizer for N(0, sigma^2), sigma^2 = 1/d.
+# ---------------------------------------------------------------------------
+
+def _phi(z: float) -> float:
+    """Standard normal density."""
+    if math.isinf(z):
+        return 0.0
+    return math.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+
+
+def gaussian_cell_mass(lo: float, hi: float) -> float:
+    """P(lo < Z <= hi) for Z ~ N(0, 1), written to avoid cancellation in the
+    tails (erfc on the side away from zero)."""
+    if lo >= 0.0:
+        return 0.5 * (math.erfc(lo / _SQRT2) - math.erfc(hi / _SQRT2))
+    if hi <= 0.0:
+        return 0.5 * (math.erfc(-hi / _SQRT2) - math.erfc(-lo / _SQRT2))
+    return 0.5 * (math.erf(hi / _SQRT2) - math.erf(lo / _SQRT2))
+
+
+def gaussian_cell_mean(lo: float, hi: float) -> float:
+    """E[Z | lo < Z <= hi] for Z ~ N(0, 1): (phi(lo) - phi(hi)) / mass."""
+    return (_phi(lo) - _phi(hi)) / gaussian_cell_mass(lo, hi)
+
+
+def lloyd_max_codebook(d: int, b: int, max_iter: int = 200000):
+    """Lloyd-Max quantizer with 2^b levels for the density N(0, 1/d).
+
+    AXELRAM (arXiv 2604.02638), Abstract: the optimal quantizer depends only
+    on the dimension d and the bit width b.  The two optimality conditions
+    (Lloyd 1982, Max 1960) are iterated to their fixed point:
+      thresholds  t_i = (c_i + c_{i+1}) / 2                (midpoint)
+      centroids   c_i = E[X | t_{i-1} < X <= t_i]           (centroid)
+    with t_{-1} = -inf and t_{2^b - 1} = +inf.  The Gaussian is log-concave,
+    so the fixed point is unique and plain iteration converges to it.
+
+    Returns (centroids[2^b], thresholds[2^b - 1]) as ascending float64 arrays.
+    """
+    if d < 1 or b < 1:
+        raise ValueError("d and b must be positive")
+    sigma = 1.0 / math.sqrt(d)
+    levels = 1 << b
+    # Start from evenly spaced points on [-2 sigma, 2 sigma]; the fixed point
+    # does not depend on the start.
+    c = np.array([sigma * (-2.0 + 4.0 * (i + 0.5) / levels) for i in range(levels)],
+                 dtype=np.float64)
+    for _ in range(max_iter):
+        t = 0.5 * (c[:-1] + c[1:])
+        edges = [-math.inf] + [float(v) for v in t] + [math.inf]
+        new = np.array([sigma * gaussian_cell_mean(edges[i] / sigma, edges[i + 1] / sigma)
+                        for i in range(levels)], dtype=np.float64)
+        delta = float(np.max(np.abs(new - c)))
+        c = new
+        if delta <= 1e-17 * sigma:
+            break
+    t = 0.5 * (c[:-1] + c[1:])
+    return c, t
+
+
+def codebook_distortion(d: int, centroids, thresholds) -> float:
+    """Mean squared error E[(X - Q(X))^2] of the quantizer for X ~ N(0, 1/d),
+    evaluated in closed form cell by cell:
+    E[(X-c)^2 ; cell] = E[X^2 ; cell] - 2c E[X ; cell] + c^2 P(cell)."""
+    sigma = 1.0 / math.sqrt(d)
+    edges = [-math.inf] + [float(v) / sigma for v in thresholds] + [math.inf]
+    total = 0.0
+    for i, cval in enumerate(centroids):
+        lo, hi = edges[i], edges[i + 1]
+        mass = gaussian_cell_mass(lo, hi)
+        first = _phi(lo) - _phi(hi)                      # E[Z ; cell]
+        lo_t = 0.0 if math.isinf(lo) else lo * _phi(lo)
+        hi_t = 0.0 if math.isinf(hi) else hi * _phi(hi)
+        second = mass + lo_t - hi_t                      # E[Z^2 ; cell]
+        cz = float(cval) / sigma
+        total += second - 2.0 * cz * first + cz * cz * mass
+    return total * sigma * sigma
+
+
+# ---------------------------------------------------------------------------
+# Orthogonal transform: sign pattern, then normalised Walsh-Hadamard.
+# ---------------------------------------------------------------------------
+
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """Dense H_d with H_d[i, j] = (-1)^popcount(i & j) (natural order)."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    i = np.arange(d, dtype=np.int64)
+    anded = i[:, None] & i[None, :]
+    parity = np.zeros_like(anded)
+    while np.any(anded):
+        parity ^= anded & 1
+        anded >>= 1
+    return np.where(parity == 0, 1.0, -1.0)
+
+
+def signs_from_bits(bits) -> np.ndarray:
+    """Sign pattern s_j = -1 where bit j is set, +1 otherwise."""
+    bits = np.asarray(bits)
+    return np.where(bits.astype(np.int64) != 0, -1.0, 1.0)
+
+
+def key_norms(keys) -> np.ndarray:
+    """Euclidean norm of each key (last axis), in float64."""
+    k = np.asarray(keys, dtype=np.float64)
+    return np.sqrt(np.sum(k * k, axis=-1))
+
+
+def rotate(x, signs) -> np.ndarray:
+    """y = H_d (s * x) / sqrt(d) along the last axis (no normalisation)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    h = sylvester_hadamard(d)
+    return ((x * np.asarray(signs, dtype=np.float64)) @ h.T) / math.sqrt(d)
+
+
+def transform_keys(keys, signs):
+    """Write-path transform: unit-normalise each key, then rotate.
+
+    Returns (y, norms).  A zero key keeps norm 0 and maps to y = 0.
+    """
+    k = np.asarray(keys, dtype=np.float64)
+    norms = key_norms(k)
+    safe = np.where(norms > 0.0, norms, 1.0)
+    unit = np.where(norms[..., None] > 0.0, k / safe[..., None], 0.0)
+    return rotate(unit, signs), norms
+
+
+def transform_queries(q, signs) -> np.ndarray:
+    """Read-path query transform q' = H_d (s * q) / sqrt(d); no normalisation."""
+    return rotate(q, signs)
+
+
+# ---------------------------------------------------------------------------
+# Scalar quantization and the packed index record.
+# ---------------------------------------------------------------------------
+
+def quantize(y, thresholds) -> np.ndarray:
+    """idx = number of thresholds strictly below y (ties take the lower cell)."""
+    y = np.asarray(y, dtype=np.float64)
+    t = np.asarray(thresholds, dtype=np.float64)
+    return np.sum(y[..., None] > t, axis=-1).astype(np.int64)
+
+
+def pack_indices(idx, b: int) -> np.ndarray:
+    """Little-endian bit stream of b-bit fields, returned as uint32 words.
+
+    idx: int array [..., d] with values in [0, 2^b).  Output [..., d*b/32].
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    d = idx.shape[-1]
+    if (d * b) % 32:
+        raise ValueError("d*b must be a multiple of 32")
+    bits = ((idx[..., :, None] >> np.arange(b)) & 1).astype(np.uint8)   # [..., d, b]
+    bits = bits.reshape(idx.shape[:-1] + (d * b,))                        # record bit j*b+r
+    as_bytes = np.packbits(bits, axis=-1, bitorder="little")              # [..., d*b/8]
+    return as_bytes.view("<u4").reshape(idx.shape[:-1] + (d * b // 32,)).astype(np.uint32)
+
+
+def unpack_indices(words, d: int, b: int) -> np.ndarray:
+    """Inverse of pack_indices."""
+    w = np.ascontiguousarray(np.asarray(words, dtype="<u4"))
+    as_bytes = w.view(np.uint8).reshape(w.shape[:-1] + (w.shape[-1] * 4,))
+    bits = np.unpackbits(as_bytes, axis=-1, bitorder="little")[..., : d * b]
+    bits = bits.reshape(w.shape[:-1] + (d, b)).astype(np.int64)
+    return np.sum(bits << np.arange(b), axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# Read path: per-query table and table-lookup accumulation.
+# ---------------------------------------------------------------------------
+
+def build_lut(qprime, centroids) -> np.ndarray:
+    """LUT[..., j, c] = q'_j * c_c."""
+    return np.asarray(qprime, dtype=np.float64)[..., :, None] * np.asarray(centroids, np.float64)
+
+
+def _gather(lut_h, idx_h):
+    # lut_h [d, L], idx_h [T, d] -> LUT[j, idx[t, j]] as [T, d]
+    d = lut_h.shape[0]
+    return lut_h[np.arange(d)[None, :], idx_h]
+
+
+def lut_scores(qprime, idx, norms, centroids) -> np.ndarray:
+    """Scores from indices: s[b, h, t] = ||k_t|| * sum_j LUT_h[j, idx[b, h//G, t, j]].
+
+    qprime [B, Hq, d]; idx [B, Hkv, T, d]; norms [B, Hkv, T].  Returns [B, Hq, T].
+    """
+    qprime = np.asarray(qprime, dtype=np.float64)
+    idx = np.asarray(idx)
+    norms = np.asarray(norms, dtype=np.float64)
+    nb, hq, _ = qprime.shape
+    hkv, t = idx.shape[1], idx.shape[2]
+    if hq % hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    g = hq // hkv
+    lut = build_lut(qprime, centroids)
+    out = np.empty((nb, hq, t), dtype=np.float64)
+    for bi in range(nb):
+        for h in range(hq):
+            kv = h // g
+            out[bi, h] = norms[bi, kv] * np.sum(_gather(lut[bi, h], idx[bi, kv]), axis=-1)
+    return out
+
+
+def score_condition(qprime, idx, norms, centroids) -> np.ndarray:
+    """||k_t|| * sum_j |LUT_h[j, idx_j]|: the scale against which the rounding
+    error of any summation order of the score is measured."""
+    qprime = np.asarray(qprime, dtype=np.float64)
+    norms = np.asarray(norms, dtype=np.float64)
+    nb, hq, _ = qprime.shape
+    hkv, t = idx.shape[1], idx.shape[2]
+    g = hq // hkv
+    lut = np.abs(build_lut(qprime, centroids))
+    out = np.empty((nb, hq, t), dtype=np.float64)
+    for bi in range(nb):
+        for h in range(hq):
+            kv = h // g
+            out[bi, h] = norms[bi, kv] * np.sum(_gather(lut[bi, h], idx[bi, kv]), axis=-1)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Whole paths.
+# ---------------------------------------------------------------------------
+
+def write_path(keys, signs, b: int):
+    """Quantize keys [..., d]: returns dict(y, norms, idx, packed)."""
+    k = np.asarray(keys, dtype=np.float64)
+    d = k.shape[-1]
+    _, thresholds = lloyd_max_codebook(d, b)
+    y, norms = transform_keys(k, signs)
+    idx = quantize(y, thresholds)
+    return {"y": y, "norms": norms, "idx": idx, "packed": pack_indices(idx, b)}
+
+
+def read_path(q, packed, norms, signs, b: int):
+    """Score queries [B, Hq, d] against packed keys [B, Hkv, T, d*b/32]."""
+    q = np.asarray(q, dtype=np.float64)
+    d = q.shape[-1]
+    centroids, _ = lloyd_max_codebook(d, b)
+    idx = unpack_indices(packed, d, b)
+    qprime = transform_queries(q, signs)
+    return lut_scores(qprime, idx, norms, centroids)
+
+
+def dequantize_then_dot(q, idx, norms, signs, centroids) -> np.ndarray:
+    """The same scores computed the long way, in the original key space:
+    reconstruct k~ = ||k|| * T^T c[idx] (T = H_d diag(s) / sqrt(d)) and take
+    q . k~.  Used only to check the table-lookup identity."""
+    q = np.asarray(q, dtype=np.float64)
+    d = q.shape[-1]
+    h = sylvester_hadamard(d)
+    s = np.asarray(signs, dtype=np.float64)
+    chat = np.asarray(centroids, np.float64)[np.asarray(idx)]            # [B,Hkv,T,d]
+    k_rec = (chat @ h) / math.sqrt(d) * s                                 # T^T c = D H c / sqrt(d)
+    k_rec = k_rec * np.asarray(norms, np.float64)[..., None]
+    nb, hq, _ = q.shape
+    hkv = k_rec.shape[1]
+    g = hq // hkv
+    out = np.empty((nb, hq, k_rec.shape[2]), dtype=np.float64)
+    for bi in range(nb):
+        for hh in range(hq):
+            out[bi, hh] = k_rec[bi, hh // g] @ q[bi, hh]
+    return out
+
+
+def multiplications_per_query(n_keys: int, d: int, b: int):
+    """Multiplications needed to score one query against n_keys keys.
+
+    Dense dot products cost n_keys * d.  The table path costs d * 2^b
+    multiplications to fill the table plus one multiplication by the stored
+    norm per key.  Returns (dense, table, ratio).
+    """
+    dense = n_keys * d
+    table = d * (1 << b) + n_keys
+    return dense, table, dense / table
