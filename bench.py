@@ -1,0 +1,185 @@
+"""Benchmark of the AXELRAM-style write + score path on one MI355X.
+
+A step is one pass of the whole hot path over the LLaMA-3.1-8B-shaped GQA
+decode cache (batch 8, 8 KV heads, 32 query heads, d = 128, b = 3, 32768
+tokens, fp16 keys): quantize every key (normalise, sign pattern, WHT,
+Lloyd-Max bucketize, pack) and score every query head against the packed
+cache (query transform, LUT in LDS, lookup-accumulate).  Inputs are resident
+in HBM before timing starts.
+
+Prints one JSON line.  Per-kernel durations come from HIP events recorded on
+the stream the kernels run on; the score kernel is also timed alone on a cold
+cache (a 1 GiB write between launches) for its HBM roofline.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "quantized keys scored/sec + achieved HBM GB/s (d=128, b=3, GQA decode)"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cold-reps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w):
+    """The fp64 oracle, as it stands, on batch element 0 of the same workload
+    (8 KV heads x 32768 tokens = 262144 keys, 32 query heads)."""
+    import numpy as np
+    import threadpoolctl
+    from oracle import axelram as A
+
+    keys = w["keys"][0:1].to(dtype=__import__("torch").float64).numpy()
+    q = w["q"][0:1].to(dtype=__import__("torch").float64).numpy()
+    s = A.signs_from_bits(w["sign_bits"])
+    t0 = time.perf_counter()
+    wr = A.write_path(keys, s, w["b"])
+    A.read_path(q, wr["packed"], wr["norms"], s, w["b"])
+    dt = time.perf_counter() - t0
+    n = keys.shape[1] * keys.shape[2]
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
+                   if p.get("user_api") == "blas"] or [1])
+    return {"value": n / dt, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"batch element 0 of 8: {n} keys (8 KV heads x 32768 tokens) quantized "
+                      f"and scored by 32 query heads, fp64 numpy, {dt:.1f} s; "
+                      f"host reports {os.cpu_count()} CPUs"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the score and write paths shard with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lut_attention_scoring_amd as axr
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating LLaMA-3.1-8B-shaped decode cache")
+    w = W.llama_decode()
+    B, Hkv, T, d = w["keys"].shape
+    Hq = w["q"].shape[1]
+    b, bits = w["b"], w["sign_bits"]
+    n = B * Hkv * T
+    keys = w["keys"].to(dev)
+    q = w["q"].to(dev)
+    packed = torch.empty(B, Hkv, T, d * b // 32, dtype=torch.int32, device=dev)
+    norms = torch.empty(B, Hkv, T, dtype=torch.float32, device=dev)
+    scores = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        axr.quantize_keys(keys, bits, b, packed=packed, norms=norms)
+        if ev is not None:
+            ev[1].record(stream)
+        axr.score(q, packed, norms, bits, b, out=scores)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    write_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    score_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+
+    # Score kernel alone on a cold cache: overwrite 1 GiB between launches.
+    log("cold-cache score timing")
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(args.cold_reps):
+        flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        axr.score(q, packed, norms, bits, b, out=scores)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    cold.sort()
+    cold_ms = cold[len(cold) // 2]
+    del flush
+
+    write_bytes_per_key = d * keys.element_size() + d * b // 8 + 4
+    score_bytes_per_key = d * b // 8 + 4 + 4 * (Hq // Hkv)
+    write_bytes = n * write_bytes_per_key
+    score_bytes = n * score_bytes_per_key
+    write_gbs = write_bytes / (write_ms * 1e-3) / 1e9
+    score_gbs = score_bytes / (score_ms * 1e-3) / 1e9
+    cold_gbs = score_bytes / (cold_ms * 1e-3) / 1e9
+    dominant = "write" if write_ms >= score_ms else "score"
+    dom_gbs = write_gbs if dominant == "write" else score_gbs
+    dom_bytes = write_bytes if dominant == "write" else score_bytes
+
+    out = {
+        "metric": METRIC,
+        "value": n / (ms_per_step * 1e-3),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "llama31_8b_gqa_decode_d128_b3", "batch": B, "kv_heads": Hkv,
+                   "q_heads": Hq, "context": T, "d": d, "b": b, "key_dtype": "f16",
+                   "keys_per_step": n},
+        "roofline": {"kernel": f"{dominant}_kernel", "bound": "hbm",
+                     "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": dom_bytes},
+        "kernels": {
+            "write": {"ms": write_ms, "keys_per_s": n / (write_ms * 1e-3),
+                      "GB_per_s": write_gbs, "frac_hbm": write_gbs / HBM_PEAK_GBS,
+                      "bytes_per_key": write_bytes_per_key},
+            "score": {"ms": score_ms, "keys_per_s": n / (score_ms * 1e-3),
+                      "GB_per_s": score_gbs, "frac_hbm": score_gbs / HBM_PEAK_GBS,
+                      "bytes_per_key": score_bytes_per_key},
+            "score_cold_cache": {"ms_median": cold_ms, "keys_per_s": n / (cold_ms * 1e-3),
+                                 "GB_per_s": cold_gbs, "frac_hbm": cold_gbs / HBM_PEAK_GBS},
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+/*
+ * axr.h -- C ABI of the AXELRAM-style LUT attention-scoring library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method: "AXELRAM: Quantize Once, Never Dequantize" (arXiv 2604.02638),
+ * Abstract.  Keys are transformed once on write by an orthogonal transform
+ * (a seeded sign pattern followed by a normalised Walsh-Hadamard transform)
+ * and scalar-quantized against a design-time codebook that depends only on
+ * the head dimension d and bit width b; queries are scored on read by table
+ * lookup, with no inverse transform.
+ *
+ * Conventions shared by every call
+ *   - All functions have C linkage, return an axr_status (0 = success) and
+ *     never throw.  On failure axr_last_error() returns a message describing
+ *     the most recent failure on the calling thread.
+ *   - Arguments are validated before any HIP call, so a rejected call leaves
+ *     the device untouched.
+ *   - Device buffers are allocated, owned and freed by the caller.  The
+ *     library allocates no device memory; it keeps only a process-wide cache
+ *     of codebooks keyed by (d, b).
+ *   - Device work is enqueued asynchronously on `stream` (a hipStream_t cast
+ *     to void*; NULL means the default stream).  Launch failures are reported
+ *     as AXR_EHIP; faults during execution surface at the caller's next
+ *     synchronisation.  The library never synchronises.
+ *   - Sign pattern: `sign_bits` is a HOST array of d/32 uint32 words; bit
+ *     (j % 32) of word (j / 32) set means s_j = -1, clear means s_j = +1.
+ *     The words are copied into kernel arguments; the array may be reused as
+ *     soon as the call returns.
+ *   - Packed index record of one key: d*b bits, little-endian bit stream:
+ *     bit r of idx_j is record bit j*b + r, record bit m is bit (m % 32) of
+ *     32-bit word (m / 32).  W = d*b/32 words per key, keys contiguous.
+ *   - Supported: d in {128, 256, 512}, b in {2, 3, 4} (axr_codebook also
+ *     accepts b = 1 and any d >= 1).
+ */
+#ifndef AXR_H
+#define AXR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum axr_status {
+  AXR_OK = 0,
+  AXR_EINVAL = -1,       /* null pointer, negative size, inconsistent shape   */
+  AXR_EUNSUPPORTED = -2, /* d, b, dtype or head layout outside what is built  */
+  AXR_EALIGN = -3,       /* a device pointer is not aligned as required       */
+  AXR_EHIP = -4          /* the HIP runtime reported an error                 */
+} axr_status;
+
+typedef enum axr_dtype { AXR_F32 = 0, AXR_F16 = 1, AXR_BF16 = 2 } axr_dtype;
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int axr_version(void);
+
+/* Message for the last non-OK return on the calling thread ("" if none).
+ * The pointer stays valid until the next axr_* call on that thread. */
+const char* axr_last_error(void);
+
+/*
+ * Design-time codebook (AXELRAM, Abstract: the optimal quantizer depends only
+ * on d and b).  Host only, no HIP call.  Computes the Lloyd-Max quantizer for
+ * the density N(0, 1/d): 2^b centroids and 2^b - 1 thresholds, each threshold
+ * the midpoint of its neighbouring centroids and each centroid the mean of
+ * N(0, 1/d) over its cell.  The quantizer is symmetric; the middle threshold
+ * is exactly 0.
+ *   centroids  : host double[2^b], written ascending
+ *   thresholds : host double[2^b - 1], written ascending
+ * Errors: AXR_EINVAL for d < 1, b outside [1, 4] or a null pointer.
+ */
+int axr_codebook(int d, int b, double* centroids, double* thresholds);
+
+/*
+ * Write path (AXELRAM, Abstract: transform on write, quantize once).
+ * For each of the n keys k (rows of `keys`):
+ *   ||k|| is stored in norms[i] (fp32, accumulated in fp32);
+ *   y = H_d (s * k) / (sqrt(d) ||k||)       (y = 0 for a zero key);
+ *   idx_j = number of codebook thresholds strictly below y_j, in [0, 2^b);
+ *   the indices are packed into packed[i*W .. i*W + W) as described above.
+ *   keys   : device, n x d elements of `dtype`, row-major, 16-byte aligned
+ *   packed : device uint32 [n][W], 16-byte aligned
+ *   norms  : device float [n], 4-byte aligned
+ * n = 0 is a no-op.  Keys of a [B][Hkv][T][d] cache are simply n = B*Hkv*T
+ * consecutive rows.  Errors: AXR_EINVAL, AXR_EUNSUPPORTED, AXR_EALIGN,
+ * AXR_EHIP.  Decisions are taken in fp32: a coordinate whose exact value lies
+ * within ~1e-7 (relative) of a threshold may fall in the neighbouring cell.
+ */
+int axr_quantize_keys(const void* keys, int dtype, int64_t n, int d, int b,
+                      const uint32_t* sign_bits, uint32_t* packed, float* norms,
+                      void* stream);
+
+/*
+ * Read path (AXELRAM, Abstract: table lookup on read, no inverse transform).
+ * For batch bi, query head h (KV head kvh = h / (Hq / Hkv)) and token t < T:
+ *   q' = H_d (s * q[bi][h]) / sqrt(d)                 (queries not normalised)
+ *   LUT[j][c] = q'_j * centroid_c
+ *   scores[bi][h][t] = norms[r] * sum_j LUT[j][idx_j(r)],  r = (bi*Hkv + kvh)*t_cap + t
+ * The sum is taken exactly in 32-bit fixed point over pairs of coordinates
+ * (a table entry holds two coordinates' products); the only roundings are the
+ * table entries (relative 2^-30 of the head's full scale) and the final fp32
+ * products, far inside 1e-5 of norms * sum_j |LUT[j][idx_j]|.
+ *   q       : device, [B][Hq][d] of q_dtype, 16-byte aligned
+ *   packed  : device uint32, [B][Hkv][t_cap][W] as written by axr_quantize_keys
+ *   norms   : device float, [B][Hkv][t_cap]
+ *   scores  : device float, [B][Hq][T] (output), 4-byte aligned
+ *   t_cap   : tokens allocated per (batch, KV head) row, t_cap >= T (pass T
+ *             for a dense cache)
+ * Requires Hq % Hkv == 0.  T = 0 or B = 0 is a no-op.  Errors: AXR_EINVAL,
+ * AXR_EUNSUPPORTED, AXR_EALIGN, AXR_EHIP.
+ */
+int axr_score(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
+              const uint32_t* sign_bits, int B, int Hq, int Hkv, int64_t T, int64_t t_cap,
+              int d, int b, float* scores, void* stream);
+
+/*
+ * Diagnostic export of the write-path transform (the same device code the
+ * quantizer runs): y[i] = H_d (s * x[i]) / sqrt(d), divided by ||x[i]|| when
+ * normalize != 0 (y = 0 for a zero row).
+ *   x : device, n x d elements of `dtype`, 16-byte aligned
+ *   y : device float [n][d], 16-byte aligned
+ * Errors: AXR_EINVAL, AXR_EUNSUPPORTED, AXR_EALIGN, AXR_EHIP.
+ */
+int axr_transform(const void* x, int dtype, int64_t n, int d, const uint32_t* sign_bits,
+                  int normalize, float* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AXR_H */

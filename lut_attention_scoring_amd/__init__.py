@@ -1,0 +1,172 @@
+"""Python binding of libaxr (AXELRAM-style LUT attention scoring for MI355X).
+
+Argument marshalling only: every step of the write and read paths runs in the
+HIP kernels of libaxr.so, reached through the C ABI declared in include/axr.h.
+PyTorch supplies device memory and the current stream.  There is no CPU
+fallback: importing this package fails if the library has not been built.
+
+Method: "AXELRAM: Quantize Once, Never Dequantize" (arXiv 2604.02638),
+Abstract.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+__all__ = [
+    "AxrError", "LIB_PATH", "lib", "version", "codebook", "sign_words",
+    "packed_words", "quantize_keys", "score", "transform",
+    "F32", "F16", "BF16",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaxr.so")
+
+F32, F16, BF16 = 0, 1, 2
+_DTYPES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+
+OK, EINVAL, EUNSUPPORTED, EALIGN, EHIP = 0, -1, -2, -3, -4
+
+
+class AxrError(RuntimeError):
+    """A libaxr call returned a non-OK status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"axr status {status}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing; build it with `python -m lut_attention_scoring_amd.build`")
+    so = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    dp = ctypes.POINTER(ctypes.c_double)
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    so.axr_version.restype = i32
+    so.axr_version.argtypes = []
+    so.axr_last_error.restype = ctypes.c_char_p
+    so.axr_last_error.argtypes = []
+    so.axr_codebook.restype = i32
+    so.axr_codebook.argtypes = [i32, i32, dp, dp]
+    so.axr_quantize_keys.restype = i32
+    so.axr_quantize_keys.argtypes = [vp, i32, i64, i32, i32, u32p, vp, vp, vp]
+    so.axr_score.restype = i32
+    so.axr_score.argtypes = [vp, i32, vp, vp, u32p, i32, i32, i32, i64, i64, i32, i32, vp, vp]
+    so.axr_transform.restype = i32
+    so.axr_transform.argtypes = [vp, i32, i64, i32, u32p, i32, vp, vp]
+    return so
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != OK:
+        raise AxrError(status, lib.axr_last_error().decode())
+
+
+def version() -> int:
+    return int(lib.axr_version())
+
+
+def codebook(d: int, b: int):
+    """Lloyd-Max centroids [2^b] and thresholds [2^b - 1] for N(0, 1/d) (host)."""
+    c = (ctypes.c_double * (1 << b))()
+    t = (ctypes.c_double * max(1, (1 << b) - 1))()
+    _check(lib.axr_codebook(d, b, c, t))
+    return np.array(c[:], dtype=np.float64), np.array(t[: (1 << b) - 1], dtype=np.float64)
+
+
+def sign_words(bits) -> np.ndarray:
+    """Sign pattern as uint32 words: bit j % 32 of word j // 32 is bits[j]."""
+    bits = np.asarray(bits).astype(np.uint32).reshape(-1)
+    if bits.size % 32:
+        raise ValueError("sign pattern length must be a multiple of 32")
+    shifts = np.arange(32, dtype=np.uint32)
+    return np.bitwise_or.reduce(bits.reshape(-1, 32) << shifts, axis=1).astype(np.uint32)
+
+
+def _words_ptr(words: np.ndarray):
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    return words, words.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _need_cuda(*tensors):
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on a GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def packed_words(d: int, b: int) -> int:
+    return d * b // 32
+
+
+def quantize_keys(keys: torch.Tensor, sign_bits, b: int, packed: torch.Tensor = None,
+                  norms: torch.Tensor = None):
+    """Write path: keys [..., d] -> (packed int32 [..., d*b/32], norms fp32 [...]).
+
+    `packed` holds the uint32 words of the record, viewed as int32."""
+    d = keys.shape[-1]
+    lead = keys.shape[:-1]
+    if packed is None:
+        packed = torch.empty(*lead, packed_words(d, b), dtype=torch.int32, device=keys.device)
+    if norms is None:
+        norms = torch.empty(*lead, dtype=torch.float32, device=keys.device)
+    _need_cuda(keys, packed, norms)
+    n = keys.numel() // d if d else 0
+    if packed.numel() != n * packed_words(d, b) or norms.numel() != n:
+        raise ValueError("packed/norms sizes do not match keys")
+    words, wp = _words_ptr(sign_words(sign_bits))
+    _check(lib.axr_quantize_keys(keys.data_ptr(), _dtype_code(keys), n, d, b, wp,
+                                 packed.data_ptr(), norms.data_ptr(), _stream(keys)))
+    return packed, norms
+
+
+def score(q: torch.Tensor, packed: torch.Tensor, norms: torch.Tensor, sign_bits, b: int,
+          T: int = None, out: torch.Tensor = None):
+    """Read path: q [B, Hq, d], packed [B, Hkv, t_cap, W], norms [B, Hkv, t_cap]
+    -> scores fp32 [B, Hq, T] (T defaults to t_cap)."""
+    B, Hq, d = q.shape
+    Bk, Hkv, t_cap, W = packed.shape
+    if Bk != B or W != packed_words(d, b) or tuple(norms.shape) != (B, Hkv, t_cap):
+        raise ValueError("q, packed and norms shapes disagree")
+    T = t_cap if T is None else int(T)
+    if out is None:
+        out = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    _need_cuda(q, packed, norms, out)
+    if tuple(out.shape) != (B, Hq, T):
+        raise ValueError("out has the wrong shape")
+    words, wp = _words_ptr(sign_words(sign_bits))
+    _check(lib.axr_score(q.data_ptr(), _dtype_code(q), packed.data_ptr(), norms.data_ptr(), wp,
+                         B, Hq, Hkv, T, t_cap, d, b, out.data_ptr(), _stream(q)))
+    return out
+
+
+def transform(x: torch.Tensor, sign_bits, normalize: bool = True, out: torch.Tensor = None):
+    """Diagnostic: y = H (s * x) / sqrt(d) (/ ||x|| if normalize), fp32 [..., d]."""
+    d = x.shape[-1]
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _need_cuda(x, out)
+    n = x.numel() // d if d else 0
+    words, wp = _words_ptr(sign_words(sign_bits))
+    _check(lib.axr_transform(x.data_ptr(), _dtype_code(x), n, d, wp, int(bool(normalize)),
+                             out.data_ptr(), _stream(x)))
+    return out

@@ -1,0 +1,156 @@
+// C-ABI layer: argument validation, error reporting, codebook preparation and
+// kernel dispatch.  Every check runs before the first HIP call, so rejected
+// calls never touch the device.  See include/axr.h for the contract.
+
+#include "axr.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "axr_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return AXR_OK;
+}
+
+bool supported_d(int d) { return d == 128 || d == 256 || d == 512; }
+bool supported_b(int b) { return b >= 2 && b <= 4; }
+bool supported_dtype(int t) { return t == AXR_F32 || t == AXR_F16 || t == AXR_BF16; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_common(int d, int b, int dtype, const uint32_t* sign_bits) {
+  if (!supported_d(d)) return fail(AXR_EUNSUPPORTED, "d=%d is not supported (128, 256, 512)", d);
+  if (!supported_b(b)) return fail(AXR_EUNSUPPORTED, "b=%d is not supported (2, 3, 4)", b);
+  if (!supported_dtype(dtype)) return fail(AXR_EUNSUPPORTED, "dtype=%d is not supported", dtype);
+  if (sign_bits == nullptr) return fail(AXR_EINVAL, "sign_bits is null");
+  return AXR_OK;
+}
+
+void fill_signs(uint32_t* dst, const uint32_t* sign_bits, int d) {
+  std::memset(dst, 0, sizeof(uint32_t) * axr::kMaxSignWords);
+  std::memcpy(dst, sign_bits, sizeof(uint32_t) * (d / 32));
+}
+
+int hip_status(int err, const char* what) {
+  if (err != 0) return fail(AXR_EHIP, "%s: HIP error %d", what, err);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int axr_version(void) { return 10000; }
+
+const char* axr_last_error(void) { return g_last_error.c_str(); }
+
+int axr_codebook(int d, int b, double* centroids, double* thresholds) {
+  if (d < 1) return fail(AXR_EINVAL, "d=%d must be >= 1", d);
+  if (b < 1 || b > 4) return fail(AXR_EINVAL, "b=%d must be in [1, 4]", b);
+  if (centroids == nullptr || thresholds == nullptr)
+    return fail(AXR_EINVAL, "centroids and thresholds must be non-null");
+  const axr::Codebook& cb = axr::cached_codebook(d, b);
+  const int levels = 1 << b;
+  for (int i = 0; i < levels; ++i) centroids[i] = cb.centroid[i];
+  for (int i = 0; i + 1 < levels; ++i) thresholds[i] = cb.threshold[i];
+  return ok();
+}
+
+static int write_common(const void* x, int dtype, int64_t n, int d, int b,
+                        const uint32_t* sign_bits, uint32_t* packed, float* norms, float* y,
+                        int mode, void* stream) {
+  int rc = check_common(d, b, dtype, sign_bits);
+  if (rc != AXR_OK) return rc;
+  if (n < 0) return fail(AXR_EINVAL, "n=%lld is negative", static_cast<long long>(n));
+  if (n == 0) return ok();
+  if (x == nullptr) return fail(AXR_EINVAL, "input pointer is null");
+  if (!aligned(x, 16)) return fail(AXR_EALIGN, "input must be 16-byte aligned");
+  if (mode == axr::kWriteQuantize) {
+    if (packed == nullptr || norms == nullptr)
+      return fail(AXR_EINVAL, "packed and norms must be non-null");
+    if (!aligned(packed, 16)) return fail(AXR_EALIGN, "packed must be 16-byte aligned");
+    if (!aligned(norms, 4)) return fail(AXR_EALIGN, "norms must be 4-byte aligned");
+  } else {
+    if (y == nullptr) return fail(AXR_EINVAL, "y is null");
+    if (!aligned(y, 16)) return fail(AXR_EALIGN, "y must be 16-byte aligned");
+  }
+  axr::WriteParams p;
+  std::memset(&p, 0, sizeof(p));
+  fill_signs(p.sign, sign_bits, d);
+  const axr::Codebook& cb = axr::cached_codebook(d, b);
+  const int half = 1 << (b - 1);
+  const double sqrt_d = std::sqrt(static_cast<double>(d));
+  for (int i = 0; i + 1 < half; ++i) p.tpos[i] = static_cast<float>(cb.threshold[half + i] * sqrt_d);
+  p.inv_sqrt_d = static_cast<float>(1.0 / sqrt_d);
+  int err = axr::launch_write(x, dtype, n, d, b, p, packed, norms, y, mode, stream);
+  return hip_status(err, "write kernel launch");
+}
+
+int axr_quantize_keys(const void* keys, int dtype, int64_t n, int d, int b,
+                      const uint32_t* sign_bits, uint32_t* packed, float* norms, void* stream) {
+  return write_common(keys, dtype, n, d, b, sign_bits, packed, norms, nullptr,
+                      axr::kWriteQuantize, stream);
+}
+
+int axr_transform(const void* x, int dtype, int64_t n, int d, const uint32_t* sign_bits,
+                  int normalize, float* y, void* stream) {
+  // b only selects a kernel instance here; the transform does not depend on it.
+  return write_common(x, dtype, n, d, 3, sign_bits, nullptr, nullptr, y,
+                      normalize ? axr::kWriteTransformNormalized : axr::kWriteTransform, stream);
+}
+
+int axr_score(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
+              const uint32_t* sign_bits, int B, int Hq, int Hkv, int64_t T, int64_t t_cap,
+              int d, int b, float* scores, void* stream) {
+  int rc = check_common(d, b, q_dtype, sign_bits);
+  if (rc != AXR_OK) return rc;
+  if (B < 0 || Hq < 0 || Hkv < 0 || T < 0)
+    return fail(AXR_EINVAL, "negative size (B=%d Hq=%d Hkv=%d T=%lld)", B, Hq, Hkv,
+                static_cast<long long>(T));
+  if (Hkv == 0 || Hq == 0) return fail(AXR_EINVAL, "Hq and Hkv must be positive");
+  if (Hq % Hkv != 0) return fail(AXR_EINVAL, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (t_cap < T) return fail(AXR_EINVAL, "t_cap=%lld is smaller than T=%lld",
+                             static_cast<long long>(t_cap), static_cast<long long>(T));
+  const int G = Hq / Hkv;
+  if (G > 64) return fail(AXR_EUNSUPPORTED, "Hq/Hkv=%d exceeds 64", G);
+  if (B == 0 || T == 0) return ok();
+  if (q == nullptr || packed == nullptr || norms == nullptr || scores == nullptr)
+    return fail(AXR_EINVAL, "q, packed, norms and scores must be non-null");
+  if (!aligned(q, 16)) return fail(AXR_EALIGN, "q must be 16-byte aligned");
+  if (!aligned(packed, 16)) return fail(AXR_EALIGN, "packed must be 16-byte aligned");
+  if (!aligned(norms, 4) || !aligned(scores, 4))
+    return fail(AXR_EALIGN, "norms and scores must be 4-byte aligned");
+  axr::ScoreParams p;
+  std::memset(&p, 0, sizeof(p));
+  fill_signs(p.sign, sign_bits, d);
+  const axr::Codebook& cb = axr::cached_codebook(d, b);
+  for (int i = 0; i < (1 << b); ++i) p.centroid[i] = static_cast<float>(cb.centroid[i]);
+  p.T = T;
+  p.t_cap = t_cap;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = G;
+  int err = axr::launch_score(q, q_dtype, packed, norms, B, d, b, p, scores, stream);
+  return hip_status(err, "score kernel launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal interfaces between the C-ABI layer (axr_api.cpp), the host
+// codebook solver (axr_codebook.cpp) and the HIP kernels (axr_kernels.hip).
+#pragma once
+
+#include <stdint.h>
+
+namespace axr {
+
+constexpr int kMaxD = 512;
+constexpr int kMaxSignWords = kMaxD / 32;
+constexpr int kMaxLevels = 16;  // 2^b for b <= 4
+
+// Lloyd-Max quantizer for N(0, 1/d) in double precision, ascending.
+struct Codebook {
+  int d = 0, b = 0;
+  double centroid[kMaxLevels];
+  double threshold[kMaxLevels - 1];
+};
+
+// Solves the Lloyd-Max conditions for N(0, 1/d) with 2^b levels (b in 1..4).
+void solve_codebook(int d, int b, Codebook* out);
+
+// Cached solution for (d, b); thread-safe.
+const Codebook& cached_codebook(int d, int b);
+
+// Kernel-side parameters (passed by value as kernel arguments).
+struct WriteParams {
+  uint32_t sign[kMaxSignWords];   // sign bits, word j/32 bit j%32
+  float tpos[kMaxLevels / 2];     // positive thresholds times sqrt(d), ascending
+  float inv_sqrt_d;
+};
+
+struct ScoreParams {
+  uint32_t sign[kMaxSignWords];
+  float centroid[kMaxLevels];     // fp32 centroids, ascending
+  int64_t T;                      // tokens scored per row
+  int64_t t_cap;                  // tokens allocated per (batch, KV head) row
+  int Hq, Hkv, G;                 // query heads, KV heads, Hq / Hkv
+  int heads_per_block;            // query heads handled by one block
+  int head_groups;                // G / heads_per_block
+  int tiles;                      // token tiles per row
+  int64_t tile_len;               // tokens per tile
+};
+
+// Launchers (return a hipError_t value as int; 0 = success).
+int launch_write(const void* keys, int dtype, int64_t n, int d, int b, const WriteParams& p,
+                 uint32_t* packed, float* norms, float* y, int mode, void* stream);
+int launch_score(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
+                 int B, int d, int b, const ScoreParams& p, float* scores, void* stream);
+
+// Mode of the write kernel: quantize (indices + norms) or transform export.
+enum WriteMode { kWriteQuantize = 0, kWriteTransform = 1, kWriteTransformNormalized = 2 };
+
+}  // namespace axr

@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: the library loads, exports what
+include/axr.h declares, solves the codebook on the host, and rejects bad
+arguments before any HIP call."""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import lut_attention_scoring_amd as axr
+from oracle import axelram as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000      # an aligned, never-dereferenced address
+SIGNS = (ctypes.c_uint32 * 16)()
+
+
+def declared_symbols():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            with open(os.path.join(ROOT, "include", fn)) as f:
+                text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+            names |= set(re.findall(r"\b(axr_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert {"axr_codebook", "axr_quantize_keys", "axr_score", "axr_transform",
+            "axr_last_error", "axr_version"} <= set(names)
+    raw = ctypes.CDLL(axr.LIB_PATH)
+    for name in names:
+        assert hasattr(raw, name), name
+
+
+def test_version():
+    assert axr.version() >= 10000
+
+
+@pytest.mark.parametrize("d", [1, 2, 64, 128, 256, 512])
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_codebook_matches_oracle(d, b):
+    c, t = axr.codebook(d, b)
+    oc, ot = A.lloyd_max_codebook(d, b)
+    sigma = 1.0 / math.sqrt(d)
+    assert np.max(np.abs(c - oc)) <= 1e-12 * sigma
+    assert np.max(np.abs(t - ot)) <= 1e-12 * sigma
+    assert t[len(t) // 2] == 0.0
+    np.testing.assert_array_equal(c, -c[::-1])
+
+
+def _status(fn, *args):
+    st = fn(*args)
+    msg = axr.lib.axr_last_error().decode()
+    return st, msg
+
+
+def test_codebook_rejects_bad_arguments():
+    c = (ctypes.c_double * 16)()
+    t = (ctypes.c_double * 15)()
+    assert _status(axr.lib.axr_codebook, 0, 3, c, t)[0] == axr.EINVAL
+    assert _status(axr.lib.axr_codebook, 128, 5, c, t)[0] == axr.EINVAL
+    assert _status(axr.lib.axr_codebook, 128, 0, c, t)[0] == axr.EINVAL
+    st, msg = _status(axr.lib.axr_codebook, 128, 3, None, t)
+    assert st == axr.EINVAL and "null" in msg
+
+
+def _q(keys=FAKE, dtype=axr.F16, n=16, d=128, b=3, signs=SIGNS, packed=FAKE, norms=FAKE):
+    return _status(axr.lib.axr_quantize_keys, keys, dtype, n, d, b, signs, packed, norms, None)
+
+
+def test_quantize_validation():
+    assert _q(d=100)[0] == axr.EUNSUPPORTED
+    assert _q(d=64)[0] == axr.EUNSUPPORTED
+    assert _q(b=1)[0] == axr.EUNSUPPORTED
+    assert _q(b=5)[0] == axr.EUNSUPPORTED
+    assert _q(dtype=9)[0] == axr.EUNSUPPORTED
+    assert _q(n=-1)[0] == axr.EINVAL
+    assert _q(signs=None)[0] == axr.EINVAL
+    assert _q(keys=None)[0] == axr.EINVAL
+    assert _q(packed=None)[0] == axr.EINVAL
+    assert _q(norms=None)[0] == axr.EINVAL
+    assert _q(keys=FAKE + 8)[0] == axr.EALIGN
+    assert _q(packed=FAKE + 4)[0] == axr.EALIGN
+    assert _q(norms=FAKE + 2)[0] == axr.EALIGN
+    st, msg = _q(d=100)
+    assert "d=100" in msg
+    # n = 0 is a no-op that never touches the device, even with null buffers
+    assert _q(n=0, keys=None, packed=None, norms=None)[0] == axr.OK
+    assert axr.lib.axr_last_error().decode() == ""
+
+
+def _s(q=FAKE, qdt=axr.F16, packed=FAKE, norms=FAKE, signs=SIGNS, B=2, Hq=8, Hkv=2, T=64,
+       t_cap=64, d=128, b=3, scores=FAKE):
+    return _status(axr.lib.axr_score, q, qdt, packed, norms, signs, B, Hq, Hkv, T, t_cap, d, b,
+                   scores, None)
+
+
+def test_score_validation():
+    assert _s(d=96)[0] == axr.EUNSUPPORTED
+    assert _s(b=7)[0] == axr.EUNSUPPORTED
+    assert _s(qdt=5)[0] == axr.EUNSUPPORTED
+    assert _s(Hq=6, Hkv=4)[0] == axr.EINVAL
+    assert _s(Hkv=0)[0] == axr.EINVAL
+    assert _s(B=-1)[0] == axr.EINVAL
+    assert _s(T=-3)[0] == axr.EINVAL
+    assert _s(t_cap=10, T=11)[0] == axr.EINVAL
+    assert _s(Hq=130, Hkv=1)[0] == axr.EUNSUPPORTED
+    assert _s(q=None)[0] == axr.EINVAL
+    assert _s(scores=None)[0] == axr.EINVAL
+    assert _s(signs=None)[0] == axr.EINVAL
+    assert _s(q=FAKE + 4)[0] == axr.EALIGN
+    assert _s(packed=FAKE + 8)[0] == axr.EALIGN
+    assert _s(scores=FAKE + 1)[0] == axr.EALIGN
+    assert _s(T=0, t_cap=0, q=None, packed=None, norms=None, scores=None)[0] == axr.OK
+    assert _s(B=0, q=None, packed=None, norms=None, scores=None)[0] == axr.OK
+
+
+def test_transform_validation():
+    f = axr.lib.axr_transform
+    assert _status(f, FAKE, axr.F32, 4, 48, SIGNS, 1, FAKE, None)[0] == axr.EUNSUPPORTED
+    assert _status(f, FAKE, axr.F32, -4, 128, SIGNS, 1, FAKE, None)[0] == axr.EINVAL
+    assert _status(f, FAKE, axr.F32, 4, 128, SIGNS, 1, None, None)[0] == axr.EINVAL
+    assert _status(f, FAKE, axr.F32, 4, 128, SIGNS, 1, FAKE + 4, None)[0] == axr.EALIGN
+    assert _status(f, None, axr.F32, 0, 128, SIGNS, 1, None, None)[0] == axr.OK
+
+
+def test_sign_words_marshalling():
+    rng = np.random.default_rng(0)
+    for d in (128, 256, 512):
+        bits = rng.integers(0, 2, d)
+        words = axr.sign_words(bits)
+        acc = sum(int(v) << j for j, v in enumerate(bits))
+        assert [int(w) for w in words] == [(acc >> (32 * k)) & 0xFFFFFFFF for k in range(d // 32)]

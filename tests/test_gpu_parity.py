@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases run the oracle on every output; they span several tiles and a
+ragged tail.  Full-size workloads run in the same launch configuration as the
+benchmark and are checked on sampled keys and tokens, which the oracle
+computes one by one."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import axelram as A
+from tests._parity import (f64, words_u32, assert_indices, assert_scores, assert_norms,
+                           TRANSFORM_ATOL)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import lut_attention_scoring_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+
+
+def axr():
+    import lut_attention_scoring_amd as m
+    return m
+
+
+def _write_and_check(keys_cpu, bits, b, label, sample=None):
+    """Quantize keys_cpu [B, Hkv, T, d] on the GPU and compare with the oracle
+    on all keys (sample=None) or on a row sample.  Returns GPU (packed, norms)."""
+    m = axr()
+    d = keys_cpu.shape[-1]
+    keys = keys_cpu.to(DEV)
+    packed, norms = m.quantize_keys(keys, bits, b)
+    y_gpu = m.transform(keys, bits, normalize=True)
+    torch.cuda.synchronize()
+    flat = keys_cpu.reshape(-1, d)
+    rows = np.arange(flat.shape[0]) if sample is None else W.sample_rows(flat.shape[0], sample)
+    k64 = f64(flat[torch.from_numpy(rows)])
+    s = A.signs_from_bits(bits)
+    c, t = A.lloyd_max_codebook(d, b)
+    y, onorm = A.transform_keys(k64, s)
+    oidx = A.quantize(y, t)
+    gw = words_u32(packed.reshape(-1, packed.shape[-1]))[rows]
+    gidx = A.unpack_indices(gw, d, b)
+    assert_indices(gidx, oidx, y, t, label)
+    assert_norms(f64(norms.reshape(-1))[rows], onorm, label)
+    ygpu = f64(y_gpu.reshape(-1, d))[rows]
+    assert np.max(np.abs(ygpu - y)) <= TRANSFORM_ATOL, label
+    return packed, norms
+
+
+def _score_and_check(q_cpu, keys_cpu, packed, norms, bits, b, label, T=None, sample=None):
+    m = axr()
+    d = q_cpu.shape[-1]
+    q = q_cpu.to(DEV)
+    Bn, Hq, _ = q_cpu.shape
+    Hkv = packed.shape[1]
+    T = packed.shape[2] if T is None else T
+    scores = m.score(q, packed, norms, bits, b, T=T)
+    qt = m.transform(q, bits, normalize=False)
+    torch.cuda.synchronize()
+    s = A.signs_from_bits(bits)
+    c, _ = A.lloyd_max_codebook(d, b)
+    qprime = A.transform_queries(f64(q_cpu), s)
+    qn = np.linalg.norm(f64(q_cpu), axis=-1)
+    assert np.all(np.abs(f64(qt) - qprime) <= TRANSFORM_ATOL * qn[..., None]), label
+    toks = np.arange(T) if sample is None else W.sample_rows(T, sample)
+    tt = torch.from_numpy(toks)
+    gidx = A.unpack_indices(words_u32(packed[:, :, tt]), d, b)
+    onorm = A.key_norms(f64(keys_cpu[:, :, tt]))
+    gs = f64(scores[:, :, tt])
+    return assert_scores(gs, qprime, gidx, onorm, c, label)
+
+
+# ---------------------------------------------------------------------------
+# Tiny workload in full: d=128, b=3, one head, 4096 fp32 keys, one query.
+# ---------------------------------------------------------------------------
+
+def test_tiny_full():
+    w = W.tiny()
+    packed, norms = _write_and_check(w["keys"], w["sign_bits"], 3, "tiny")
+    _score_and_check(w["q"], w["keys"], packed, norms, w["sign_bits"], 3, "tiny")
+
+
+# ---------------------------------------------------------------------------
+# Small, ragged, multi-tile cases over every (d, b, dtype).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("b", [2, 3, 4])
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_write_ragged(d, b, dtype):
+    rng = np.random.default_rng(d * 10 + b)
+    n = 3 * 64 + 37                                         # not a multiple of any block
+    k = rng.standard_normal((1, 1, n, d)) * np.exp(rng.standard_normal(d))
+    keys = torch.from_numpy(k.astype(np.float32)).to(dtype)
+    _write_and_check(keys, W.sign_bits(d), b, f"write d={d} b={b} {dtype}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_score_ragged_gqa(G, b):
+    d, Bn, Hkv, T, t_cap = 128, 2, 2, 1237, 1300
+    rng = np.random.default_rng(100 * G + b)
+    keys = torch.from_numpy((rng.standard_normal((Bn, Hkv, t_cap, d)) * 3.0).astype(np.float32)
+                            ).to(torch.float16)
+    q = torch.from_numpy(rng.standard_normal((Bn, Hkv * G, d)).astype(np.float32)).to(torch.float16)
+    bits = W.sign_bits(d)
+    packed, norms = _write_and_check(keys, bits, b, f"gqa G={G}")
+    _score_and_check(q, keys, packed, norms, bits, b, f"score G={G} b={b}", T=T)
+
+
+@pytest.mark.parametrize("d,b", [(256, 2), (256, 3), (256, 4), (512, 2), (512, 3), (512, 4)])
+def test_score_wide_heads(d, b):
+    Bn, Hkv, G, T = 1, 2, 4, 777
+    rng = np.random.default_rng(d + b)
+    keys = torch.from_numpy(rng.standard_normal((Bn, Hkv, T, d)).astype(np.float32)).to(torch.bfloat16)
+    q = torch.from_numpy(rng.standard_normal((Bn, Hkv * G, d)).astype(np.float32)).to(torch.bfloat16)
+    bits = W.sign_bits(d)
+    packed, norms = _write_and_check(keys, bits, b, f"wide d={d}")
+    _score_and_check(q, keys, packed, norms, bits, b, f"wide score d={d} b={b}")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases.
+# ---------------------------------------------------------------------------
+
+def test_empty_and_single():
+    m = axr()
+    bits = W.sign_bits(128)
+    keys = torch.empty(0, 128, dtype=torch.float16, device=DEV)
+    packed, norms = m.quantize_keys(keys, bits, 3)
+    assert packed.shape == (0, 12) and norms.shape == (0,)
+    q = torch.ones(1, 4, 128, dtype=torch.float16, device=DEV)
+    out = m.score(q, torch.empty(1, 1, 0, 12, dtype=torch.int32, device=DEV),
+                  torch.empty(1, 1, 0, device=DEV), bits, 3)
+    assert out.shape == (1, 4, 0)
+    one = torch.randn(1, 1, 1, 128, generator=torch.Generator().manual_seed(3)).to(torch.float16)
+    p1, n1 = _write_and_check(one, bits, 3, "single key")
+    _score_and_check(q.cpu(), one, p1, n1, bits, 3, "single key score")
+
+
+def test_zero_norm_keys():
+    m = axr()
+    bits = W.sign_bits(128)
+    keys = torch.zeros(1, 1, 70, 128, dtype=torch.float32)
+    keys[0, 0, 3] = 1.0
+    for b in (2, 3, 4):
+        packed, norms = _write_and_check(keys, bits, b, f"zero keys b={b}")
+        idx = A.unpack_indices(words_u32(packed[0, 0]), 128, b)
+        zero_rows = [i for i in range(70) if i != 3]
+        assert np.all(idx[zero_rows] == 2 ** (b - 1) - 1)
+        assert float(norms[0, 0, 0]) == 0.0
+        q = torch.randn(1, 2, 128, generator=torch.Generator().manual_seed(b))
+        sc = m.score(q.to(DEV), packed, norms, bits, b)
+        torch.cuda.synchronize()
+        assert torch.all(sc[0, :, zero_rows] == 0.0)
+
+
+def test_extreme_magnitudes_fp32():
+    rng = np.random.default_rng(77)
+    k = rng.standard_normal((1, 1, 300, 128))
+    k[0, 0, :100] *= 1e18
+    k[0, 0, 100:200] *= 1e-18
+    keys = torch.from_numpy(k.astype(np.float32))
+    bits = W.sign_bits(128)
+    packed, norms = _write_and_check(keys, bits, 3, "extreme magnitudes")
+    q = torch.from_numpy(rng.standard_normal((1, 3, 128)).astype(np.float32))
+    _score_and_check(q, keys, packed, norms, bits, 3, "extreme magnitudes score")
+
+
+def test_score_is_deterministic_and_tile_independent():
+    m = axr()
+    w = W.llama_decode(B=1, Hkv=2, Hq=8, T=5000)
+    keys = w["keys"].to(DEV)
+    q = w["q"].to(DEV)
+    packed, norms = m.quantize_keys(keys, w["sign_bits"], 3)
+    a = m.score(q, packed, norms, w["sign_bits"], 3)
+    b_ = m.score(q, packed, norms, w["sign_bits"], 3)
+    # a prefix of the cache (different tiling) gives the same leading scores
+    c = m.score(q, packed, norms, w["sign_bits"], 3, T=1234)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b_)
+    assert torch.equal(a[:, :, :1234], c)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads.  Reduced sizes run the same recipe everywhere; full
+# sizes run in the benchmark's launch configuration on sampled outputs.
+# ---------------------------------------------------------------------------
+
+def test_llama_decode_reduced_full_check():
+    w = W.llama_decode(B=2, Hkv=8, Hq=32, T=600)
+    packed, norms = _write_and_check(w["keys"], w["sign_bits"], 3, "llama reduced")
+    _score_and_check(w["q"], w["keys"], packed, norms, w["sign_bits"], 3, "llama reduced")
+
+
+def test_llama_decode_full_size_sampled():
+    w = W.llama_decode()
+    packed, norms = _write_and_check(w["keys"], w["sign_bits"], 3, "llama full", sample=8192)
+    _score_and_check(w["q"], w["keys"], packed, norms, w["sign_bits"], 3, "llama full",
+                     sample=1024)
+
+
+def test_qwen_all_layers_reduced():
+    for layer in range(W.QWEN_LAYERS):
+        w = W.qwen_layer(layer, B=2, T=256)
+        packed, norms = _write_and_check(w["keys"], w["sign_bits"], 4, f"qwen layer {layer}")
+        _score_and_check(w["q"], w["keys"], packed, norms, w["sign_bits"], 4,
+                         f"qwen layer {layer}")
+
+
+@pytest.mark.parametrize("layer", [0, 35])
+def test_qwen_layer_full_size_sampled(layer):
+    w = W.qwen_layer(layer)
+    packed, norms = _write_and_check(w["keys"], w["sign_bits"], 4, f"qwen full {layer}",
+                                     sample=4096)
+    _score_and_check(w["q"], w["keys"], packed, norms, w["sign_bits"], 4, f"qwen full {layer}",
+                     sample=512)
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_long_context_full_size_sampled(b):
+    w = W.long_context(b=b)
+    packed, norms = _write_and_check(w["keys"], w["sign_bits"], b, f"long b={b}", sample=4096)
+    _score_and_check(w["q"], w["keys"], packed, norms, w["sign_bits"], b, f"long b={b}",
+                     sample=256)
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_write_sweep_full_size_sampled(d, b):
+    w = W.write_sweep(d=d, b=b)
+    _write_and_check(w["keys"], w["sign_bits"], b, f"sweep d={d} b={b}", sample=4096)
