@@ -41,25 +41,27 @@ def parse():
 
 
 def cpu_baseline(w):
-    """The fp64 oracle, as it stands, on batch element 0 of the same workload
-    (8 KV heads x 32768 tokens = 262144 keys, 32 query heads)."""
+    """The fp64 oracle, as it stands, on batch elements [0, 4) of the same
+    workload (4 x 8 KV heads x 32768 tokens = 1048576 keys, 32 query heads)."""
     import numpy as np
     import threadpoolctl
     from oracle import axelram as A
 
-    keys = w["keys"][0:1].to(dtype=__import__("torch").float64).numpy()
-    q = w["q"][0:1].to(dtype=__import__("torch").float64).numpy()
+    import torch
+    nb = 4
+    keys = w["keys"][0:nb].to(dtype=torch.float64).numpy()
+    q = w["q"][0:nb].to(dtype=torch.float64).numpy()
     s = A.signs_from_bits(w["sign_bits"])
     t0 = time.perf_counter()
     wr = A.write_path(keys, s, w["b"])
     A.read_path(q, wr["packed"], wr["norms"], s, w["b"])
     dt = time.perf_counter() - t0
-    n = keys.shape[1] * keys.shape[2]
+    n = keys.shape[0] * keys.shape[1] * keys.shape[2]
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
                    if p.get("user_api") == "blas"] or [1])
     return {"value": n / dt, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"batch element 0 of 8: {n} keys (8 KV heads x 32768 tokens) quantized "
-                      f"and scored by 32 query heads, fp64 numpy, {dt:.1f} s; "
+            "sample": f"batch elements 0-3 of 8: {n} keys (4 x 8 KV heads x 32768 tokens) "
+                      f"quantized and scored by 32 query heads each, fp64 numpy, {dt:.1f} s; "
                       f"host reports {os.cpu_count()} CPUs"}
 
 
@@ -90,32 +92,40 @@ def main():
     scores = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         axr.quantize_keys(keys, bits, b, packed=packed, norms=norms)
-        if ev is not None:
-            ev[1].record(stream)
         axr.score(q, packed, norms, bits, b, out=scores)
-        if ev is not None:
-            ev[2].record(stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(events[k])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    write_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    score_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+
+    def per_launch_ms(fn, reps):
+        """Average duration of `reps` back-to-back launches of fn, from HIP
+        events recorded on the stream the kernels run on."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    log("per-kernel timing")
+    write_ms = per_launch_ms(lambda: axr.quantize_keys(keys, bits, b, packed=packed, norms=norms),
+                             args.steps)
+    score_ms = per_launch_ms(lambda: axr.score(q, packed, norms, bits, b, out=scores), args.steps)
 
     # Score kernel alone on a cold cache: overwrite 1 GiB between launches.
     log("cold-cache score timing")

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libaxr.so")
 
-SOURCES = ["axr_api.cpp", "axr_codebook.cpp", "axr_kernels.hip"]
+SOURCES = ["axr_api.cpp", "axr_codebook.cpp", "axr_write.hip", "axr_score.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -1,0 +1,53 @@
+// Device helpers shared by the write and score kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace axr {
+
+// Value held by lane (lane ^ M) inside aligned groups of up to 16 lanes.
+// xor 1 / xor 2 are DPP quad permutations, xor 8 is DPP row_ror:8 inside a
+// 16-lane row; xor 4 has no DPP control on this architecture and uses
+// ds_swizzle's bitmask mode.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v) {
+  const int iv = static_cast<int>(v);
+  if constexpr (M == 1) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (M == 2) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (M == 4) {
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(iv, (4 << 10) | 0x1F));
+  } else {
+    static_assert(M == 8, "lane distance must be 1, 2, 4 or 8");
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, false));
+  }
+}
+
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  return __uint_as_float(lane_xor_u32<M>(__float_as_uint(v)));
+}
+
+// Right rotation of an N-word little-endian bit string by r bits, 0 <= r < 32.
+template <int N>
+__device__ __forceinline__ void rotate_right(uint32_t (&w)[N], uint32_t r) {
+  uint32_t out[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) out[i] = __builtin_amdgcn_alignbit(w[(i + 1) % N], w[i], r);
+#pragma unroll
+  for (int i = 0; i < N; ++i) w[i] = out[i];
+}
+
+// Bits [pos, pos + width) of an N-word little-endian bit string; pos and
+// width are compile-time after unrolling, width <= 32.
+template <int N>
+__device__ __forceinline__ uint32_t bits_at(const uint32_t (&w)[N], int pos, int width) {
+  const int wi = pos >> 5, sh = pos & 31;
+  const uint32_t mask = width == 32 ? 0xFFFFFFFFu : ((1u << width) - 1u);
+  if (sh + width <= 32) return (w[wi] >> sh) & mask;
+  return __builtin_amdgcn_alignbit(w[(wi + 1) % N], w[wi], sh) & mask;
+}
+
+}  // namespace axr

@@ -1,0 +1,473 @@
+// Read-path kernel for gfx950: attention scores straight from packed
+// quantization indices, by table lookup, with no inverse transform.
+//
+// "AXELRAM: Quantize Once, Never Dequantize" (arXiv 2604.02638), Abstract:
+// the query is turned once into a table of products q'_j * c_k and each key's
+// score is its stored norm times the sum of the table entries its indices
+// select.
+//
+// Design (one block = up to 8 query heads of one (batch, KV head) row, one
+// tile of tokens):
+//   * prologue: q' = H (s * q) / sqrt(d) for the block's heads (LDS), a
+//     power-of-two fixed-point scale per head, and a table of int32 group
+//     sums in LDS.  A group is P = 2 adjacent coordinates (a 2b-bit field of
+//     the packed record, so no index reshuffling) or P = 1 when the pair
+//     table would not fit.  One table entry is 16 bytes: the group sum for 4
+//     heads.  Integer accumulation is exact, so the score's only roundings
+//     are the table entries (2^-30 of the head's full scale) and the final
+//     fp32 multiply.
+//   * loop: a key is read by LPK = d/32 adjacent lanes, lane u owning the
+//     32 coordinates [32u, 32u+32) = b words of the record, so a wave reads
+//     a contiguous span of records.  Each lane looks up its groups, the
+//     lanes of a key sum their partial results across lanes, and each lane
+//     writes the scores of its heads.
+//   * LDS banks: 16-byte reads are conflict-free when the 16 lanes of a
+//     quarter-wave touch 16 different 16-byte columns of a 256-byte row.  The
+//     table puts group v of lane-chunk u in column (v + KPG*u) mod 16 and each
+//     lane walks its groups starting at an offset k (its key's slot in the
+//     quarter-wave), after rotating its record by k fields, so the 16 lanes
+//     always hit 16 distinct columns whatever the indices are.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "axr.h"
+#include "axr_device.h"
+#include "axr_internal.h"
+
+namespace axr {
+namespace {
+
+// k + s[lane ^ M] as one v_add_u32 with a DPP source (M = 1 or 2, quad
+// permutations).  The leading s_nop 1 gives the two wait states a DPP read
+// needs after the VALU write of its source.
+template <int M>
+__device__ __forceinline__ uint32_t dpp_add(uint32_t k, uint32_t s) {
+  if constexpr (M == 1) {
+    asm("s_nop 1\n\tv_add_u32_dpp %0, %1, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "+v"(k) : "v"(s));
+  } else {
+    static_assert(M == 2, "quad distances only");
+    asm("s_nop 1\n\tv_add_u32_dpp %0, %1, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+        : "+v"(k) : "v"(s));
+  }
+  return k;
+}
+
+// Sum of four per-lane partial sums a[0..3] over the 4 lanes of a quad,
+// scattered: lane u of the quad returns the total of a[u].
+__device__ __forceinline__ uint32_t quad_reduce_scatter(const uint32_t (&a)[4], bool hi1,
+                                                        bool hi2) {
+  const uint32_t s0 = hi2 ? a[0] : a[2], s1 = hi2 ? a[1] : a[3];
+  uint32_t k0 = hi2 ? a[2] : a[0], k1 = hi2 ? a[3] : a[1];
+  k0 = dpp_add<2>(k0, s0);
+  k1 = dpp_add<2>(k1, s1);
+  const uint32_t sx = hi1 ? k0 : k1;
+  const uint32_t kx = hi1 ? k1 : k0;
+  return dpp_add<1>(kx, sx);
+}
+
+template <int D, int BITS, int P>
+struct ScoreShape {
+  static constexpr int LPK = D / 32;            // lanes per key
+  static constexpr int KPG = 16 / LPK;          // keys per 16-lane group
+  static constexpr int KPW = 64 / LPK;          // keys per wave
+  static constexpr int WL = BITS;               // record words per lane (32 coords)
+  static constexpr int W = D * BITS / 32;       // record words per key
+  static constexpr int FB = P * BITS;           // field bits per group
+  static constexpr int NE = 1 << FB;            // entries per group
+  static constexpr int NV = 32 / P;             // groups per lane
+  static constexpr int ROWS_U = (NV / 16) * NE; // 256-byte rows per lane chunk
+  static constexpr int TBYTES = 256 * LPK * ROWS_U;  // bytes per 4-head table
+};
+
+constexpr int PD = 2;                // record batches in flight per wave
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit dword format
+
+// (field << 8) for the width-bit field at bit pos of an N-word bit string,
+// ready to be or-ed into a table address (bits 8 .. 8 + width).
+template <int N>
+__device__ __forceinline__ uint32_t field_shl8(const uint32_t (&w)[N], int pos, int width) {
+  const int wi = pos >> 5, sh = pos & 31;
+  const uint32_t mask = ((1u << width) - 1u) << 8;
+  if (sh + width <= 32) {
+    if (sh >= 8) return (w[wi] >> (sh - 8)) & mask;
+    return (w[wi] << (8 - sh)) & mask;
+  }
+  return __builtin_amdgcn_alignbit(w[(wi + 1) % N], w[wi], sh - 8) & mask;
+}
+
+// The same bits before masking (the caller masks with ((1 << width) - 1) << 8).
+template <int N>
+__device__ __forceinline__ uint32_t field_shl8_raw(const uint32_t (&w)[N], int pos, int width) {
+  const int wi = pos >> 5, sh = pos & 31;
+  if (sh + width <= 32) {
+    if (sh >= 8) return w[wi] >> (sh - 8);
+    return w[wi] << (8 - sh);
+  }
+  return __builtin_amdgcn_alignbit(w[(wi + 1) % N], w[wi], sh - 8);
+}
+
+// (a & mask) | c in one instruction (the compiler would otherwise emit an and
+// and an add for disjoint bits).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(c));
+  return r;
+}
+
+template <int WL>
+__device__ __forceinline__ void buffer_load_words(uint32_t (&dst)[WL], __amdgpu_buffer_rsrc_t r,
+                                                  uint32_t voff, uint32_t soff) {
+  if constexpr (WL == 2) {
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    dst[0] = v.x; dst[1] = v.y;
+  } else if constexpr (WL == 3) {
+    typedef uint32_t v3u __attribute__((ext_vector_type(3)));
+    const v3u v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+    dst[0] = v.x; dst[1] = v.y; dst[2] = v.z;
+  } else {
+    static_assert(WL == 4, "2, 3 or 4 record words per lane");
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+  }
+}
+
+template <int D, int BITS, int P, int NT, int NTHREADS>
+__global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict__ q, int qdt,
+                                                       const uint32_t* __restrict__ packed,
+                                                       const float* __restrict__ norms,
+                                                       float* __restrict__ scores,
+                                                       ScoreParams prm) {
+  using S = ScoreShape<D, BITS, P>;
+  constexpr int GB = 4 * NT;                    // heads per block (some may be padding)
+  constexpr int L = 1 << BITS;                  // codebook levels
+  constexpr int HL = L / 2;
+  // Static LDS (compile-time offsets fold into the read instructions):
+  // NT tables of S::TBYTES bytes, q' [GB][D] and the head scales.
+  __shared__ int4 lut[NT * (S::TBYTES / 16)];
+  __shared__ float qs[GB][D];
+  __shared__ float hscale[GB], hinv[GB];
+
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x % prm.tiles;
+  const int hg = (blockIdx.x / prm.tiles) % prm.head_groups;
+  const int row = blockIdx.x / (prm.tiles * prm.head_groups);
+  const int bi = row / prm.Hkv;
+  const int kvh = row % prm.Hkv;
+  const int h0 = kvh * prm.G + hg * GB;         // first query head of the block
+  const int nvalid = min(GB, prm.G - hg * GB);  // heads of this block that exist
+  const int wave = tid / 64, lane = tid % 64;
+  const int u = lane % S::LPK;                  // 32-coordinate chunk of the key
+  const int kw = lane / S::LPK;                 // key index in the wave
+  constexpr int KPB = (NTHREADS / 64) * S::KPW;  // keys per block iteration
+  constexpr uint32_t REC_BYTES = S::W * 4;
+  const int64_t t0 = static_cast<int64_t>(tile) * prm.tile_len;
+  const int64_t t1 = (t0 + prm.tile_len < prm.T) ? t0 + prm.tile_len : prm.T;
+  const size_t rowbase = static_cast<size_t>(row) * prm.t_cap;
+
+  // Records and norms of this (batch, KV head) row through raw buffer
+  // resources limited to the T scored tokens: loads past the end return 0,
+  // so prefetching needs no clamping.
+  const __amdgpu_buffer_rsrc_t rrec = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(packed + rowbase * S::W), 0,
+      static_cast<int>(static_cast<uint32_t>(prm.T) * REC_BYTES), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rnrm = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(norms + rowbase), 0, static_cast<int>(static_cast<uint32_t>(prm.T) * 4u),
+      kRsrcWord3);
+  const int64_t tw = t0 + wave * S::KPW;        // first token of this wave's first batch
+  const uint32_t vrec = static_cast<uint32_t>(tw + kw) * REC_BYTES + u * (S::WL * 4);
+  const uint32_t vnrm = static_cast<uint32_t>(tw + kw) * 4u;
+
+  // Issue the first PD batches now, so that HBM is busy while the table is built.
+  uint32_t wq[PD][S::WL];
+  float nq[PD];
+#pragma unroll
+  for (int pd = 0; pd < PD; ++pd) {
+    buffer_load_words<S::WL>(wq[pd], rrec, vrec, pd * KPB * REC_BYTES);
+    nq[pd] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rnrm, vnrm, pd * KPB * 4u, 0));
+  }
+
+  // 1. q' = H (s * q) / sqrt(d) for head g by wave g, in registers: lane l
+  //    holds coordinates l + 64 r; butterflies over r in registers and over
+  //    the lane bits by cross-lane exchange.  The same wave sums |q'_j| (in a
+  //    fixed order, so every block of a row gets the same scale) and picks
+  //    the head's fixed-point scale 2^e with sum_j |q'_j| max|c| 2^e < 2^30.
+  if (wave < GB) {
+    constexpr int R = D / 64;
+    const int g = wave;
+    float v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int j = lane + 64 * r;
+      float x = 0.0f;
+      if (g < nvalid) {
+        const size_t off = (static_cast<size_t>(bi) * prm.Hq + h0 + g) * D + j;
+        if (qdt == AXR_F32) {
+          x = static_cast<const float*>(q)[off];
+        } else if (qdt == AXR_F16) {
+          x = __half2float(static_cast<const __half*>(q)[off]);
+        } else {
+          x = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(q)[off]) << 16);
+        }
+        if ((prm.sign[j >> 5] >> (j & 31)) & 1u) x = -x;
+      }
+      v[r] = x;
+    }
+#pragma unroll
+    for (int h = 1; h < R; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        if ((i & h) == 0) {
+          const float a = v[i], b = v[i + h];
+          v[i] = a + b;
+          v[i + h] = a - b;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float pv = __shfl_xor(v[r], m);
+        v[r] = (lane & m) ? pv - v[r] : v[r] + pv;
+      }
+    }
+    const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(D));
+    float sa = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      v[r] *= inv_sqrt_d;
+      qs[g][lane + 64 * r] = v[r];
+      sa += fabsf(v[r]);
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) sa += __shfl_xor(sa, m);
+    if (lane == 0) {
+      const float cmax = fabsf(prm.centroid[L - 1]);
+      const float f = sa * cmax * 1.0001f;
+      int e = 0;
+      if (f > 0.0f) frexpf(f, &e);              // f < 2^e
+      int sh = 30 - e;
+      sh = sh > 126 ? 126 : (sh < -126 ? -126 : sh);
+      hscale[g] = ldexpf(1.0f, sh);
+      hinv[g] = ldexpf(1.0f, -sh);
+    }
+  }
+  __syncthreads();
+
+  // 2. the tables, one 16-byte entry (4 heads) per (lane chunk u, group v,
+  //    field f).  The codebook is symmetric (c[L-1-k] = -c[k]), so each task
+  //    rounds the per-coordinate products once and writes mirrored entries by
+  //    negation; a pair entry is the sum of its two rounded coordinate terms.
+  {
+    auto slot_of = [](int uu, int vv, int ff) {
+      return 16 * (uu * S::ROWS_U + (vv / 16) * S::NE + ff) + ((vv + S::KPG * uu) & 15);
+    };
+    constexpr int TASKS = NT * S::LPK * S::NV * HL;
+    for (int task = tid; task < TASKS; task += NTHREADS) {
+      const int flo = task % HL;
+      const int vv = (task / HL) % S::NV;
+      const int uu = (task / (HL * S::NV)) % S::LPK;
+      const int t4 = task / (HL * S::NV * S::LPK);
+      const int j = 32 * uu + P * vv;
+      int4* tab = lut + t4 * (S::TBYTES / 16);
+      int a[4];
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh)
+        a[hh] = __float2int_rn(qs[4 * t4 + hh][j] * prm.centroid[flo] * hscale[4 * t4 + hh]);
+      if constexpr (P == 1) {
+        tab[slot_of(uu, vv, flo)] = make_int4(a[0], a[1], a[2], a[3]);
+        tab[slot_of(uu, vv, L - 1 - flo)] = make_int4(-a[0], -a[1], -a[2], -a[3]);
+      } else {
+        int bq[4][HL];
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+#pragma unroll
+          for (int k = 0; k < HL; ++k)
+            bq[hh][k] = __float2int_rn(qs[4 * t4 + hh][j + 1] * prm.centroid[k] *
+                                       hscale[4 * t4 + hh]);
+        }
+#pragma unroll
+        for (int fhi = 0; fhi < L; ++fhi) {
+          int bv[4];
+#pragma unroll
+          for (int hh = 0; hh < 4; ++hh) bv[hh] = fhi < HL ? bq[hh][fhi] : -bq[hh][L - 1 - fhi];
+          tab[slot_of(uu, vv, flo | (fhi << BITS))] =
+              make_int4(a[0] + bv[0], a[1] + bv[1], a[2] + bv[2], a[3] + bv[3]);
+          tab[slot_of(uu, vv, (L - 1 - flo) | (fhi << BITS))] =
+              make_int4(bv[0] - a[0], bv[1] - a[1], bv[2] - a[2], bv[3] - a[3]);
+        }
+      }
+    }
+  }
+
+  // per-step table offsets of this lane (independent of the key)
+  const int kslot = (lane / S::LPK) % S::KPG;   // key slot in the 16-lane group
+  uint32_t boff[S::NV];
+#pragma unroll
+  for (int st = 0; st < S::NV; ++st) {
+    const int vv = (st + kslot) % S::NV;
+    boff[st] = static_cast<uint32_t>(
+        256 * (u * S::ROWS_U + (vv / 16) * S::NE) + 16 * ((vv + S::KPG * u) & 15));
+  }
+  const uint32_t rot = static_cast<uint32_t>(kslot * S::FB);
+  const bool hi1 = (u & 1) != 0, hi2 = (u & 2) != 0;
+  const uint32_t fmask = ((1u << S::FB) - 1u) << 8;
+  __syncthreads();
+  float ginv[GB];                               // 2^-e per head (this lane's heads)
+#pragma unroll
+  for (int g = 0; g < GB; ++g) ginv[g] = hinv[g];
+
+  // 3. stream the tile, keeping PD batches of records in flight
+  const char* lut_bytes = reinterpret_cast<const char*>(lut);
+  for (int64_t tb0 = tw; tb0 < t1; tb0 += PD * KPB) {
+#pragma unroll
+    for (int pd = 0; pd < PD; ++pd) {
+      const int64_t tb = tb0 + static_cast<int64_t>(pd) * KPB;
+      if (tb >= t1) break;                      // wave-uniform
+      const int64_t t = tb + kw;
+      uint32_t w[S::WL];
+#pragma unroll
+      for (int i = 0; i < S::WL; ++i) w[i] = wq[pd][i];
+      const float nk = nq[pd];
+      {
+        const uint32_t sb = static_cast<uint32_t>(tb - tw) + PD * KPB;  // batch PD ahead
+        buffer_load_words<S::WL>(wq[pd], rrec, vrec, sb * REC_BYTES);
+        nq[pd] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               rnrm, vnrm, sb * 4u, 0));
+      }
+      rotate_right<S::WL>(w, rot);
+
+      uint32_t acc[GB];
+#pragma unroll
+      for (int g = 0; g < GB; ++g) acc[g] = 0u;
+#pragma unroll
+      for (int st = 0; st < S::NV; ++st) {
+        const uint32_t addr = and_or(field_shl8_raw<S::WL>(w, st * S::FB, S::FB), fmask, boff[st]);
+#pragma unroll
+        for (int t4 = 0; t4 < NT; ++t4) {
+          const int4 e = *reinterpret_cast<const int4*>(lut_bytes + addr + t4 * S::TBYTES);
+          acc[4 * t4 + 0] += static_cast<uint32_t>(e.x);
+          acc[4 * t4 + 1] += static_cast<uint32_t>(e.y);
+          acc[4 * t4 + 2] += static_cast<uint32_t>(e.z);
+          acc[4 * t4 + 3] += static_cast<uint32_t>(e.w);
+        }
+      }
+      const bool valid = t < t1;
+      if constexpr (S::LPK == 4) {
+        // lane u of the key ends with head u (and u + 4 when NT = 2)
+#pragma unroll
+        for (int t4 = 0; t4 < NT; ++t4) {
+          const uint32_t a4[4] = {acc[4 * t4], acc[4 * t4 + 1], acc[4 * t4 + 2], acc[4 * t4 + 3]};
+          const uint32_t tot = quad_reduce_scatter(a4, hi1, hi2);
+          const int g = 4 * t4 + u;
+          if (valid && g < nvalid) {
+            scores[(static_cast<size_t>(bi) * prm.Hq + h0 + g) * prm.T + t] =
+                nk * (static_cast<float>(static_cast<int32_t>(tot)) * ginv[g]);
+          }
+        }
+      } else {
+        // sum over the LPK lanes of the key (exact integer sums)
+#pragma unroll
+        for (int g = 0; g < GB; ++g) {
+          acc[g] += lane_xor_u32<1>(acc[g]);
+          acc[g] += lane_xor_u32<2>(acc[g]);
+          if constexpr (S::LPK >= 8) acc[g] += lane_xor_u32<4>(acc[g]);
+          if constexpr (S::LPK >= 16) acc[g] += lane_xor_u32<8>(acc[g]);
+        }
+        if (valid) {
+#pragma unroll
+          for (int g = 0; g < GB; ++g) {
+            if (g % S::LPK == u && g < nvalid) {
+              const float sc = static_cast<float>(static_cast<int32_t>(acc[g])) * ginv[g];
+              scores[(static_cast<size_t>(bi) * prm.Hq + h0 + g) * prm.T + t] = nk * sc;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+constexpr int kLdsBudget = 128 * 1024;
+
+template <int D, int BITS, int P>
+constexpr int table_bytes(int NT) { return NT * ScoreShape<D, BITS, P>::TBYTES; }
+
+// Pairs when the pair table fits the LDS budget, else single coordinates.
+template <int D, int BITS, int NT>
+constexpr int pick_p() { return table_bytes<D, BITS, 2>(NT) <= kLdsBudget ? 2 : 1; }
+
+template <int D, int BITS, int NT>
+constexpr bool fits() { return table_bytes<D, BITS, pick_p<D, BITS, NT>()>(NT) <= kLdsBudget; }
+
+template <int D, int BITS, int NT>
+int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms, int B,
+              ScoreParams p, float* scores, hipStream_t s) {
+  constexpr int P = pick_p<D, BITS, NT>();
+  constexpr int tbytes = table_bytes<D, BITS, P>(NT);
+  constexpr int bytes = tbytes + 4 * NT * D * 4 + 2 * 4 * NT * 4;  // + q' + scales
+  static_assert(tbytes <= kLdsBudget, "table exceeds the LDS budget");
+  // 1024-thread blocks (two fit per CU below 76 KiB of tables), except the
+  // single-coordinate two-table case whose registers need 512-thread blocks.
+  constexpr int NTHREADS = (P == 1 && NT == 2) ? 512 : 1024;
+  static_assert(bytes <= 160 * 1024, "LDS per block exceeded");
+  using S = ScoreShape<D, BITS, P>;
+  constexpr int KPB = (NTHREADS / 64) * S::KPW;
+  p.heads_per_block = 4 * NT;
+  p.head_groups = (p.G + 4 * NT - 1) / (4 * NT);
+  const int64_t rows = static_cast<int64_t>(B) * p.Hkv * p.head_groups;
+  const int64_t per_cu = bytes <= 80 * 1024 ? 2 : 1;
+  const int64_t target = 256 * per_cu;          // one wave of resident blocks
+  int64_t tiles = (target + rows - 1) / rows;
+  int64_t tile_len = (p.T + tiles - 1) / tiles;
+  if (tile_len < 4 * KPB) tile_len = 4 * KPB;   // amortise the table build
+  tile_len = (tile_len + KPB - 1) / KPB * KPB;
+  tiles = (p.T + tile_len - 1) / tile_len;
+  p.tiles = static_cast<int>(tiles);
+  p.tile_len = tile_len;
+  const int64_t grid = rows * tiles;
+  if (grid > 0x7FFFFFFF) return static_cast<int>(hipErrorInvalidValue);
+  hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS>), dim3(static_cast<unsigned>(grid)),
+                     dim3(NTHREADS), 0, s, q, qdt, packed, norms, scores, p);
+  return static_cast<int>(hipGetLastError());
+}
+
+// Eight heads per block when G >= 8 and both tables fit; otherwise four.
+template <int D, int BITS>
+int launch_b(const void* q, int qdt, const uint32_t* packed, const float* norms, int B,
+             const ScoreParams& p, float* scores, hipStream_t s) {
+  if constexpr (fits<D, BITS, 2>()) {
+    if (p.G >= 8) return launch_nt<D, BITS, 2>(q, qdt, packed, norms, B, p, scores, s);
+  }
+  return launch_nt<D, BITS, 1>(q, qdt, packed, norms, B, p, scores, s);
+}
+
+template <int D>
+int launch_d(const void* q, int qdt, const uint32_t* packed, const float* norms, int B, int b,
+             const ScoreParams& p, float* scores, hipStream_t s) {
+  switch (b) {
+    case 2: return launch_b<D, 2>(q, qdt, packed, norms, B, p, scores, s);
+    case 3: return launch_b<D, 3>(q, qdt, packed, norms, B, p, scores, s);
+    default: return launch_b<D, 4>(q, qdt, packed, norms, B, p, scores, s);
+  }
+}
+
+}  // namespace
+
+int launch_score(const void* q, int q_dtype, const uint32_t* packed, const float* norms, int B,
+                 int d, int b, const ScoreParams& p, float* scores, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (d) {
+    case 128: return launch_d<128>(q, q_dtype, packed, norms, B, b, p, scores, s);
+    case 256: return launch_d<256>(q, q_dtype, packed, norms, B, b, p, scores, s);
+    default: return launch_d<512>(q, q_dtype, packed, norms, B, b, p, scores, s);
+  }
+}
+
+}  // namespace axr
