@@ -9,7 +9,7 @@ in HBM before timing starts.
 
 Prints one JSON line.  Per-kernel durations come from HIP events recorded on
 the stream the kernels run on; the score kernel is also timed alone on a cold
-cache (a 1 GiB write between launches) for its HBM roofline.
+cache (2 GiB of reads between launches) for its HBM roofline.
 """
 
 import argparse
@@ -24,6 +24,31 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "quantized keys scored/sec + achieved HBM GB/s (d=128, b=3, GQA decode)"
+CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
+
+# HBM bytes per launch on this workload from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes (profiles/*_llama31_8b_decode_d128_b3.md): FETCH_SIZE x 2.0
+# + WRITE_SIZE x 1.0, factors from a 2 GiB read and a 2 GiB fill in the same
+# runs.  Valid only for the kernel sources they were taken on (SHA-1 of the
+# files below); otherwise traffic is reported as null.
+COUNTER_TRAFFIC = {
+    "write": {"sources": ["axr_write.hip", "axr_device.h", "axr_internal.h"],
+              "sha1": "15188abfe85a0b0666c86a57e7f983f9025d8a6c",
+              "bytes": (262190.2 * 2.0 + 106815.9) * 1024},
+    "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
+              "sha1": "745673f0709c5c7f587f85ef6a477cdfc7ac23b7",
+              "bytes": (53558.0 * 2.0 + 32775.7) * 1024},
+}
+
+
+def counter_traffic(kernel):
+    import hashlib
+    entry = COUNTER_TRAFFIC[kernel]
+    h = hashlib.sha1()
+    for name in entry["sources"]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return entry["bytes"] if h.hexdigest() == entry["sha1"] else None
 
 
 def log(msg):
@@ -127,12 +152,15 @@ def main():
                              args.steps)
     score_ms = per_launch_ms(lambda: axr.score(q, packed, norms, bits, b, out=scores), args.steps)
 
-    # Score kernel alone on a cold cache: overwrite 1 GiB between launches.
+    # Score kernel alone on a cold cache: read 2 GiB between launches, which
+    # evicts the 136 MiB working set from the 256 MB Infinity Cache and L2
+    # without leaving dirty lines behind.
     log("cold-cache score timing")
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    flush = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
     cold = []
     for _ in range(args.cold_reps):
-        flush.fill_(1.0)
+        torch.sum(flush, dim=0, out=sink)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         axr.score(q, packed, norms, bits, b, out=scores)
@@ -141,7 +169,7 @@ def main():
         cold.append(e0.elapsed_time(e1))
     cold.sort()
     cold_ms = cold[len(cold) // 2]
-    del flush
+    del flush, sink
 
     write_bytes_per_key = d * keys.element_size() + d * b // 8 + 4
     score_bytes_per_key = d * b // 8 + 4 + 4 * (Hq // Hkv)
@@ -172,15 +200,18 @@ def main():
                    "keys_per_step": n},
         "roofline": {"kernel": f"{dominant}_kernel", "bound": "hbm",
                      "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic(dominant),
                      "bytes_per_launch": dom_bytes},
         "kernels": {
             "write": {"ms": write_ms, "keys_per_s": n / (write_ms * 1e-3),
                       "GB_per_s": write_gbs, "frac_hbm": write_gbs / HBM_PEAK_GBS,
-                      "bytes_per_key": write_bytes_per_key},
+                      "bytes_per_key": write_bytes_per_key,
+                      "traffic": counter_traffic("write")},
             "score": {"ms": score_ms, "keys_per_s": n / (score_ms * 1e-3),
                       "GB_per_s": score_gbs, "frac_hbm": score_gbs / HBM_PEAK_GBS,
-                      "bytes_per_key": score_bytes_per_key},
+                      "bytes_per_key": score_bytes_per_key,
+                      "traffic": counter_traffic("score")},
             "score_cold_cache": {"ms_median": cold_ms, "keys_per_s": n / (cold_ms * 1e-3),
                                  "GB_per_s": cold_gbs, "frac_hbm": cold_gbs / HBM_PEAK_GBS},
         },

@@ -106,8 +106,9 @@ int axr_quantize_keys(const void* keys, int dtype, int64_t n, int d, int b,
  *   scores  : device float, [B][Hq][T] (output), 4-byte aligned
  *   t_cap   : tokens allocated per (batch, KV head) row, t_cap >= T (pass T
  *             for a dense cache)
- * Requires Hq % Hkv == 0.  T = 0 or B = 0 is a no-op.  Errors: AXR_EINVAL,
- * AXR_EUNSUPPORTED, AXR_EALIGN, AXR_EHIP.
+ * Requires Hq % Hkv == 0, Hq / Hkv <= 64 and T * d * b / 8 < 2^31 (the
+ * records of one row are addressed with 32-bit offsets).  T = 0 or B = 0 is a
+ * no-op.  Errors: AXR_EINVAL, AXR_EUNSUPPORTED, AXR_EALIGN, AXR_EHIP.
  */
 int axr_score(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
               const uint32_t* sign_bits, int B, int Hq, int Hkv, int64_t T, int64_t t_cap,

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <climits>
 #include <cstring>
 #include <string>
 
@@ -132,6 +133,10 @@ int axr_score(const void* q, int q_dtype, const uint32_t* packed, const float* n
                              static_cast<long long>(t_cap), static_cast<long long>(T));
   const int G = Hq / Hkv;
   if (G > 64) return fail(AXR_EUNSUPPORTED, "Hq/Hkv=%d exceeds 64", G);
+  // one (batch, KV head) row of records is addressed with 32-bit offsets
+  if (T > 0 && T * static_cast<int64_t>(d) * b / 8 > INT32_MAX)
+    return fail(AXR_EUNSUPPORTED, "T=%lld tokens exceed 2 GiB of records per row",
+                static_cast<long long>(T));
   if (B == 0 || T == 0) return ok();
   if (q == nullptr || packed == nullptr || norms == nullptr || scores == nullptr)
     return fail(AXR_EINVAL, "q, packed, norms and scores must be non-null");

@@ -83,6 +83,7 @@ struct ScoreShape {
 };
 
 constexpr int PD = 2;                // record batches in flight per wave
+constexpr int IL = 1;                // batches processed together
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit dword format
 
 // (field << 8) for the width-bit field at bit pos of an N-word bit string,
@@ -170,13 +171,14 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   const size_t rowbase = static_cast<size_t>(row) * prm.t_cap;
 
   // Records and norms of this (batch, KV head) row through raw buffer
-  // resources limited to the T scored tokens: loads past the end return 0,
-  // so prefetching needs no clamping.
+  // resources that end at this block's last token: loads past the tile return
+  // 0 without touching memory, so prefetching needs no clamping and fetches
+  // nothing beyond the tile.
   const __amdgpu_buffer_rsrc_t rrec = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(packed + rowbase * S::W), 0,
-      static_cast<int>(static_cast<uint32_t>(prm.T) * REC_BYTES), kRsrcWord3);
+      static_cast<int>(static_cast<uint32_t>(t1) * REC_BYTES), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rnrm = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(norms + rowbase), 0, static_cast<int>(static_cast<uint32_t>(prm.T) * 4u),
+      const_cast<float*>(norms + rowbase), 0, static_cast<int>(static_cast<uint32_t>(t1) * 4u),
       kRsrcWord3);
   const int64_t tw = t0 + wave * S::KPW;        // first token of this wave's first batch
   const uint32_t vrec = static_cast<uint32_t>(tw + kw) * REC_BYTES + u * (S::WL * 4);
@@ -323,69 +325,84 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 #pragma unroll
   for (int g = 0; g < GB; ++g) ginv[g] = hinv[g];
 
-  // 3. stream the tile, keeping PD batches of records in flight
+  // 3. stream the tile, keeping PD batches of records in flight and working
+  //    on IL of them at once (independent lookups interleave in the LDS
+  //    queue).  A batch past the tile end is computed but not stored.
   const char* lut_bytes = reinterpret_cast<const char*>(lut);
   for (int64_t tb0 = tw; tb0 < t1; tb0 += PD * KPB) {
 #pragma unroll
-    for (int pd = 0; pd < PD; ++pd) {
-      const int64_t tb = tb0 + static_cast<int64_t>(pd) * KPB;
-      if (tb >= t1) break;                      // wave-uniform
-      const int64_t t = tb + kw;
-      uint32_t w[S::WL];
+    for (int pd0 = 0; pd0 < PD; pd0 += IL) {
+      if (tb0 + static_cast<int64_t>(pd0) * KPB >= t1) break;   // wave-uniform
+      uint32_t w[IL][S::WL];
+      float nk[IL];
 #pragma unroll
-      for (int i = 0; i < S::WL; ++i) w[i] = wq[pd][i];
-      const float nk = nq[pd];
-      {
-        const uint32_t sb = static_cast<uint32_t>(tb - tw) + PD * KPB;  // batch PD ahead
+      for (int il = 0; il < IL; ++il) {
+        const int pd = pd0 + il;
+#pragma unroll
+        for (int i = 0; i < S::WL; ++i) w[il][i] = wq[pd][i];
+        nk[il] = nq[pd];
+        const uint32_t sb =
+            static_cast<uint32_t>(tb0 - tw) + static_cast<uint32_t>(pd + PD) * KPB;
         buffer_load_words<S::WL>(wq[pd], rrec, vrec, sb * REC_BYTES);
         nq[pd] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                rnrm, vnrm, sb * 4u, 0));
+        rotate_right<S::WL>(w[il], rot);
       }
-      rotate_right<S::WL>(w, rot);
 
-      uint32_t acc[GB];
+      uint32_t acc[IL][GB];
 #pragma unroll
-      for (int g = 0; g < GB; ++g) acc[g] = 0u;
+      for (int il = 0; il < IL; ++il)
+#pragma unroll
+        for (int g = 0; g < GB; ++g) acc[il][g] = 0u;
 #pragma unroll
       for (int st = 0; st < S::NV; ++st) {
-        const uint32_t addr = and_or(field_shl8_raw<S::WL>(w, st * S::FB, S::FB), fmask, boff[st]);
 #pragma unroll
-        for (int t4 = 0; t4 < NT; ++t4) {
-          const int4 e = *reinterpret_cast<const int4*>(lut_bytes + addr + t4 * S::TBYTES);
-          acc[4 * t4 + 0] += static_cast<uint32_t>(e.x);
-          acc[4 * t4 + 1] += static_cast<uint32_t>(e.y);
-          acc[4 * t4 + 2] += static_cast<uint32_t>(e.z);
-          acc[4 * t4 + 3] += static_cast<uint32_t>(e.w);
-        }
-      }
-      const bool valid = t < t1;
-      if constexpr (S::LPK == 4) {
-        // lane u of the key ends with head u (and u + 4 when NT = 2)
+        for (int il = 0; il < IL; ++il) {
+          const uint32_t addr =
+              and_or(field_shl8_raw<S::WL>(w[il], st * S::FB, S::FB), fmask, boff[st]);
 #pragma unroll
-        for (int t4 = 0; t4 < NT; ++t4) {
-          const uint32_t a4[4] = {acc[4 * t4], acc[4 * t4 + 1], acc[4 * t4 + 2], acc[4 * t4 + 3]};
-          const uint32_t tot = quad_reduce_scatter(a4, hi1, hi2);
-          const int g = 4 * t4 + u;
-          if (valid && g < nvalid) {
-            scores[(static_cast<size_t>(bi) * prm.Hq + h0 + g) * prm.T + t] =
-                nk * (static_cast<float>(static_cast<int32_t>(tot)) * ginv[g]);
+          for (int t4 = 0; t4 < NT; ++t4) {
+            const int4 e = *reinterpret_cast<const int4*>(lut_bytes + addr + t4 * S::TBYTES);
+            acc[il][4 * t4 + 0] += static_cast<uint32_t>(e.x);
+            acc[il][4 * t4 + 1] += static_cast<uint32_t>(e.y);
+            acc[il][4 * t4 + 2] += static_cast<uint32_t>(e.z);
+            acc[il][4 * t4 + 3] += static_cast<uint32_t>(e.w);
           }
         }
-      } else {
-        // sum over the LPK lanes of the key (exact integer sums)
+      }
 #pragma unroll
-        for (int g = 0; g < GB; ++g) {
-          acc[g] += lane_xor_u32<1>(acc[g]);
-          acc[g] += lane_xor_u32<2>(acc[g]);
-          if constexpr (S::LPK >= 8) acc[g] += lane_xor_u32<4>(acc[g]);
-          if constexpr (S::LPK >= 16) acc[g] += lane_xor_u32<8>(acc[g]);
-        }
-        if (valid) {
+      for (int il = 0; il < IL; ++il) {
+        const int64_t t = tb0 + static_cast<int64_t>(pd0 + il) * KPB + kw;
+        const bool valid = t < t1;
+        if constexpr (S::LPK == 4) {
+          // lane u of the key ends with head u (and u + 4 when NT = 2)
+#pragma unroll
+          for (int t4 = 0; t4 < NT; ++t4) {
+            const uint32_t a4[4] = {acc[il][4 * t4], acc[il][4 * t4 + 1], acc[il][4 * t4 + 2],
+                                    acc[il][4 * t4 + 3]};
+            const uint32_t tot = quad_reduce_scatter(a4, hi1, hi2);
+            const int g = 4 * t4 + u;
+            if (valid && g < nvalid) {
+              scores[(static_cast<size_t>(bi) * prm.Hq + h0 + g) * prm.T + t] =
+                  nk[il] * (static_cast<float>(static_cast<int32_t>(tot)) * ginv[g]);
+            }
+          }
+        } else {
+          // sum over the LPK lanes of the key (exact integer sums)
 #pragma unroll
           for (int g = 0; g < GB; ++g) {
-            if (g % S::LPK == u && g < nvalid) {
-              const float sc = static_cast<float>(static_cast<int32_t>(acc[g])) * ginv[g];
-              scores[(static_cast<size_t>(bi) * prm.Hq + h0 + g) * prm.T + t] = nk * sc;
+            acc[il][g] += lane_xor_u32<1>(acc[il][g]);
+            acc[il][g] += lane_xor_u32<2>(acc[il][g]);
+            if constexpr (S::LPK >= 8) acc[il][g] += lane_xor_u32<4>(acc[il][g]);
+            if constexpr (S::LPK >= 16) acc[il][g] += lane_xor_u32<8>(acc[il][g]);
+          }
+          if (valid) {
+#pragma unroll
+            for (int g = 0; g < GB; ++g) {
+              if (g % S::LPK == u && g < nvalid) {
+                const float sc = static_cast<float>(static_cast<int32_t>(acc[il][g])) * ginv[g];
+                scores[(static_cast<size_t>(bi) * prm.Hq + h0 + g) * prm.T + t] = nk[il] * sc;
+              }
             }
           }
         }

@@ -21,8 +21,9 @@
 // Quantization compares z = H(s*k) (before the 1/(sqrt(d)||k||) scale)
 // against thresholds multiplied by sqrt(d)||k||, by binary search on |z|
 // over the positive thresholds of the symmetric codebook, then mirrors for
-// z <= 0 (a zero coordinate, e.g. of a zero key, takes the cell just below
-// the middle threshold 0, as a value equal to a threshold does).
+// z <= 0 (a coordinate equal to +0, and every coordinate of a zero key, takes
+// the cell just below the middle threshold 0, as a value equal to a
+// threshold does).
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -102,24 +103,52 @@ __device__ __forceinline__ void reg_stage(float (&x)[32]) {
   }
 }
 
-// Positive-side cell index HALF + #{positive thresholds < a}, a = |z|.
+// Positive-side cell index minus one: HALF - 1 + #{positive thresholds < a},
+// a = |z|.  (The +1 is added once per packed word; written this way the
+// compare feeds a carry-in add instead of a select.)
 template <int BITS>
-__device__ __forceinline__ uint32_t positive_cell(float a, const float (&S)[8]) {
-  constexpr uint32_t HALF = 1u << (BITS - 1);
+__device__ __forceinline__ uint32_t positive_cell_m1(float a, const float (&S)[8]) {
+  constexpr uint32_t B = (1u << (BITS - 1)) - 1u;
   if constexpr (BITS == 2) {
-    return a > S[0] ? HALF + 1u : HALF;
+    return B + (a > S[0] ? 1u : 0u);
   } else if constexpr (BITS == 3) {
     const bool c1 = a > S[1];
     const float t = c1 ? S[2] : S[0];
-    return (c1 ? HALF + 2u : HALF) + (a > t ? 1u : 0u);
+    return (c1 ? B + 2u : B) + (a > t ? 1u : 0u);
   } else {
     static_assert(BITS == 4, "b must be 2, 3 or 4");
     const bool c1 = a > S[3];
     const float t2 = c1 ? S[5] : S[1];
     const bool c2 = a > t2;
     const float t3 = c1 ? (c2 ? S[6] : S[4]) : (c2 ? S[2] : S[0]);
-    return (c1 ? HALF + 4u : HALF) + (c2 ? 2u : 0u) + (a > t3 ? 1u : 0u);
+    return (c1 ? B + 4u : B) + (c2 ? 2u : 0u) + (a > t3 ? 1u : 0u);
   }
+}
+
+// Constant with a 1 in the lowest bit of every BITS-bit field that lies
+// wholly inside record word i (the fields of 32 coordinates span BITS words;
+// fields split across two words are excluded).
+template <int BITS>
+__device__ __forceinline__ constexpr uint32_t ones_word(int i) {
+  uint32_t w = 0u;
+  for (int r = 0; r < 32; ++r) {
+    const int pos = r * BITS;
+    if ((pos >> 5) == i && (pos & 31) + BITS <= 32) w |= 1u << (pos & 31);
+  }
+  return w;
+}
+
+// Record word i of a key whose 32 coordinates all take cell HALF - 1.
+template <int BITS>
+__device__ __forceinline__ constexpr uint32_t zero_key_word(int i) {
+  const uint32_t v = (1u << (BITS - 1)) - 1u;
+  uint32_t w = 0u;
+  for (int r = 0; r < 32; ++r) {
+    const int pos = r * BITS;
+    if ((pos >> 5) == i) w |= v << (pos & 31);
+    if ((pos >> 5) + 1 == i && (pos & 31) + BITS > 32) w |= v >> (32 - (pos & 31));
+  }
+  return w;
 }
 
 template <int DT>
@@ -192,10 +221,11 @@ __global__ __launch_bounds__(kBlock) void write_kernel(const void* __restrict__ 
         const half2_v h2 = __builtin_bit_cast(half2_v, r);
         ss = __builtin_amdgcn_fdot2(h2, h2, ss, false);
         const uint32_t f = r ^ xm[i];
-        const float lo = __half2float(__ushort_as_half(static_cast<unsigned short>(f & 0xFFFFu)));
-        const float hi = __half2float(__ushort_as_half(static_cast<unsigned short>(f >> 16)));
-        x[2 * i] = lo + hi;
-        x[2 * i + 1] = lo - hi;
+        // first butterfly straight from the two fp16 halves: lo + hi, lo - hi
+        asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]"
+            : "=v"(x[2 * i]) : "v"(f));
+        asm("v_fma_mix_f32 %0, %1, -1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]"
+            : "=v"(x[2 * i + 1]) : "v"(f));
       }
     } else if constexpr (DT == AXR_BF16) {
 #pragma unroll
@@ -238,27 +268,43 @@ __global__ __launch_bounds__(kBlock) void write_kernel(const void* __restrict__ 
       float S[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) S[i] = P[i] * nrm;
-      // words = P ^ N: P holds the positive-side cells, N flips all bits of
-      // the fields whose coordinate is <= 0 (mirror to the negative side)
+      // words = (P + ONES) ^ N: P holds the positive-side cells minus one,
+      // ONES adds 1 to every field inside a word (no carries: a positive-side
+      // cell fits its field), N flips all bits of the fields whose coordinate
+      // is <= 0 (mirror to the negative side).
       constexpr uint32_t FLIP = (1u << BITS) - 1u;
       uint32_t Pw[BITS], Nw[BITS];
 #pragma unroll
       for (int i = 0; i < BITS; ++i) Pw[i] = Nw[i] = 0u;
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
-        const uint32_t mpos = positive_cell<BITS>(fabsf(x[r]), S);
-        const uint32_t neg = x[r] > 0.0f ? 0u : 0xFFFFFFFFu;
+        const uint32_t mm = positive_cell_m1<BITS>(fabsf(x[r]), S);
+        // all ones when z <= 0: the sign of the signed integer bits(z) - 1
+        // (+0 -> -1, positives -> >= 0, negatives -> < 0).  Only -0 reads as
+        // positive; it arises from zero inputs, and a zero key is handled
+        // below.
+        const uint32_t nm = static_cast<uint32_t>(
+            static_cast<int32_t>(__float_as_uint(x[r]) - 1u) >> 31);
         const int pos = r * BITS, wi = pos >> 5, sh = pos & 31;
-        Pw[wi] |= mpos << sh;
-        Nw[wi] |= neg & (FLIP << sh);
-        if (sh + BITS > 32) {
-          Pw[wi + 1] |= mpos >> (32 - sh);
-          Nw[wi + 1] |= neg & (FLIP >> (32 - sh));
+        if (sh + BITS <= 32) {
+          Pw[wi] |= mm << sh;
+          Nw[wi] |= nm & (FLIP << sh);
+        } else {
+          // a field split across two words gets its +1 here (a carry out of
+          // the lower word would be lost)
+          const uint32_t m1 = mm + 1u;
+          Pw[wi] |= m1 << sh;
+          Nw[wi] |= nm & (FLIP << sh);
+          Pw[wi + 1] |= m1 >> (32 - sh);
+          Nw[wi + 1] |= nm & (FLIP >> (32 - sh));
         }
       }
+      // A zero key has z = +-0 everywhere: every coordinate sits on the middle
+      // threshold and takes the cell below it (HALF - 1 in every field).
       uint32_t words[BITS];
 #pragma unroll
-      for (int i = 0; i < BITS; ++i) words[i] = Pw[i] ^ Nw[i];
+      for (int i = 0; i < BITS; ++i)
+        words[i] = nrm > 0.0f ? (Pw[i] + ones_word<BITS>(i)) ^ Nw[i] : zero_key_word<BITS>(i);
       if (valid) {
         uint32_t* dst = packed + static_cast<size_t>(key) * W + u * BITS;
         if constexpr (BITS == 2) {

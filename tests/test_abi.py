@@ -136,3 +136,9 @@ def test_sign_words_marshalling():
         words = axr.sign_words(bits)
         acc = sum(int(v) << j for j, v in enumerate(bits))
         assert [int(w) for w in words] == [(acc >> (32 * k)) & 0xFFFFFFFF for k in range(d // 32)]
+
+
+def test_score_rejects_rows_beyond_32bit_offsets():
+    # 2^31 bytes of d=128, b=3 records is 44.7M tokens per row
+    st, msg = _s(T=45_000_000, t_cap=45_000_000)
+    assert st == axr.EUNSUPPORTED and "2 GiB" in msg
