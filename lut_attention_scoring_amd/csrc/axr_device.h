@@ -6,10 +6,10 @@
 
 namespace axr {
 
-// Value held by lane (lane ^ M) inside aligned groups of up to 16 lanes.
-// xor 1 / xor 2 are DPP quad permutations, xor 8 is DPP row_ror:8 inside a
-// 16-lane row; xor 4 has no DPP control on this architecture and uses
-// ds_swizzle's bitmask mode.
+// Value held by lane (lane ^ M).  xor 1 / xor 2 are DPP quad permutations,
+// xor 8 is DPP row_ror:8 inside a 16-lane row; xor 4 and xor 16 have no DPP
+// control on this architecture and use ds_swizzle's bitmask mode (inside 32
+// lanes); xor 32 crosses the half-waves through ds_bpermute.
 template <int M>
 __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v) {
   const int iv = static_cast<int>(v);
@@ -17,11 +17,13 @@ __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v) {
     return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, false));
   } else if constexpr (M == 2) {
     return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, false));
-  } else if constexpr (M == 4) {
-    return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(iv, (4 << 10) | 0x1F));
-  } else {
-    static_assert(M == 8, "lane distance must be 1, 2, 4 or 8");
+  } else if constexpr (M == 4 || M == 16) {
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(iv, (M << 10) | 0x1F));
+  } else if constexpr (M == 8) {
     return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, false));
+  } else {
+    static_assert(M == 32, "lane distance must be 1, 2, 4, 8, 16 or 32");
+    return static_cast<uint32_t>(__shfl_xor(iv, 32));
   }
 }
 

@@ -55,17 +55,23 @@ __device__ __forceinline__ uint32_t dpp_add(uint32_t k, uint32_t s) {
   return k;
 }
 
-// Sum of four per-lane partial sums a[0..3] over the 4 lanes of a quad,
-// scattered: lane u of the quad returns the total of a[u].
-__device__ __forceinline__ uint32_t quad_reduce_scatter(const uint32_t (&a)[4], bool hi1,
-                                                        bool hi2) {
-  const uint32_t s0 = hi2 ? a[0] : a[2], s1 = hi2 ? a[1] : a[3];
-  uint32_t k0 = hi2 ? a[2] : a[0], k1 = hi2 ? a[3] : a[1];
-  k0 = dpp_add<2>(k0, s0);
-  k1 = dpp_add<2>(k1, s1);
-  const uint32_t sx = hi1 ? k0 : k1;
-  const uint32_t kx = hi1 ? k1 : k0;
-  return dpp_add<1>(kx, sx);
+// Sum over the 4 lanes of a quad, scattered: a[i] of lane u holds head
+// (u ^ i), so lane u ends with the total of head u.  Each step keeps the half
+// whose heads match the lane's own bit and sends the other half, which in the
+// partner's numbering is exactly the half it keeps: no selects are needed.
+__device__ __forceinline__ uint32_t quad_reduce_scatter(const uint32_t (&a)[4]) {
+  const uint32_t k0 = dpp_add<2>(a[0], a[2]);   // heads u and u^1 (+ partner u^2)
+  const uint32_t k1 = dpp_add<2>(a[1], a[3]);
+  return dpp_add<1>(k0, k1);                    // head u
+}
+
+// Butterfly stage of the query transform across lanes at distance M: the
+// lane with bit M clear keeps a + b, its partner a - b (lane holds R values).
+template <int M, int R>
+__device__ __forceinline__ void qlane_stage(float (&v)[R], int lane) {
+  const float sgn = (lane & M) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] = fmaf(v[r], sgn, lane_xor<M>(v[r]));
 }
 
 template <int D, int BITS, int P>
@@ -152,6 +158,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   __shared__ int4 lut[NT * (S::TBYTES / 16)];
   __shared__ float qs[GB][D];
   __shared__ float hscale[GB], hinv[GB];
+  __shared__ float cent[16];
 
   const int tid = threadIdx.x;
   const int tile = blockIdx.x % prm.tiles;
@@ -184,25 +191,15 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   const uint32_t vrec = static_cast<uint32_t>(tw + kw) * REC_BYTES + u * (S::WL * 4);
   const uint32_t vnrm = static_cast<uint32_t>(tw + kw) * 4u;
 
-  // Issue the first PD batches now, so that HBM is busy while the table is built.
-  uint32_t wq[PD][S::WL];
-  float nq[PD];
-#pragma unroll
-  for (int pd = 0; pd < PD; ++pd) {
-    buffer_load_words<S::WL>(wq[pd], rrec, vrec, pd * KPB * REC_BYTES);
-    nq[pd] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           rnrm, vnrm, pd * KPB * 4u, 0));
-  }
-
   // 1. q' = H (s * q) / sqrt(d) for head g by wave g, in registers: lane l
   //    holds coordinates l + 64 r; butterflies over r in registers and over
   //    the lane bits by cross-lane exchange.  The same wave sums |q'_j| (in a
   //    fixed order, so every block of a row gets the same scale) and picks
   //    the head's fixed-point scale 2^e with sum_j |q'_j| max|c| 2^e < 2^30.
+  constexpr int R = D / 64;
+  float v[R];
   if (wave < GB) {
-    constexpr int R = D / 64;
     const int g = wave;
-    float v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int j = lane + 64 * r;
@@ -220,6 +217,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
       }
       v[r] = x;
     }
+  }
+  if (tid < L) cent[tid] = prm.centroid[tid];
+  if (wave < GB) {
+    const int g = wave;
 #pragma unroll
     for (int h = 1; h < R; h <<= 1) {
 #pragma unroll
@@ -231,14 +232,12 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
         }
       }
     }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float pv = __shfl_xor(v[r], m);
-        v[r] = (lane & m) ? pv - v[r] : v[r] + pv;
-      }
-    }
+    qlane_stage<1>(v, lane);
+    qlane_stage<2>(v, lane);
+    qlane_stage<4>(v, lane);
+    qlane_stage<8>(v, lane);
+    qlane_stage<16>(v, lane);
+    qlane_stage<32>(v, lane);
     const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(D));
     float sa = 0.0f;
 #pragma unroll
@@ -247,8 +246,12 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
       qs[g][lane + 64 * r] = v[r];
       sa += fabsf(v[r]);
     }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) sa += __shfl_xor(sa, m);
+    sa += lane_xor<1>(sa);
+    sa += lane_xor<2>(sa);
+    sa += lane_xor<4>(sa);
+    sa += lane_xor<8>(sa);
+    sa += lane_xor<16>(sa);
+    sa += lane_xor<32>(sa);
     if (lane == 0) {
       const float cmax = fabsf(prm.centroid[L - 1]);
       const float f = sa * cmax * 1.0001f;
@@ -262,49 +265,57 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   }
   __syncthreads();
 
+  // Issue the first PD batches of record loads now: after the query loads
+  // (which start the critical path and should not queue behind them) and
+  // before the table build, which they overlap.
+  uint32_t wq[PD][S::WL];
+  float nq[PD];
+#pragma unroll
+  for (int pd = 0; pd < PD; ++pd) {
+    buffer_load_words<S::WL>(wq[pd], rrec, vrec, pd * KPB * REC_BYTES);
+    nq[pd] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rnrm, vnrm, pd * KPB * 4u, 0));
+  }
+
   // 2. the tables, one 16-byte entry (4 heads) per (lane chunk u, group v,
-  //    field f).  The codebook is symmetric (c[L-1-k] = -c[k]), so each task
-  //    rounds the per-coordinate products once and writes mirrored entries by
-  //    negation; a pair entry is the sum of its two rounded coordinate terms.
+  //    field f).  The codebook is symmetric (c[L-1-k] = -c[k]), so the entry
+  //    of the fully mirrored field is the negation: each task rounds the
+  //    coordinate terms once and writes an entry and its mirror.  A pair
+  //    entry is the sum of its two rounded coordinate terms.
   {
     auto slot_of = [](int uu, int vv, int ff) {
       return 16 * (uu * S::ROWS_U + (vv / 16) * S::NE + ff) + ((vv + S::KPG * uu) & 15);
     };
-    constexpr int TASKS = NT * S::LPK * S::NV * HL;
+    constexpr int HALF_NE = S::NE / 2;           // fields with the top bit clear
+    constexpr int TASKS = NT * S::LPK * S::NV * HALF_NE;
+    // group index fastest: the 16 lanes of a quarter-wave write 16 distinct
+    // LDS columns
     for (int task = tid; task < TASKS; task += NTHREADS) {
-      const int flo = task % HL;
-      const int vv = (task / HL) % S::NV;
-      const int uu = (task / (HL * S::NV)) % S::LPK;
-      const int t4 = task / (HL * S::NV * S::LPK);
+      const int vv = task % S::NV;
+      const int f = (task / S::NV) % HALF_NE;
+      const int uu = (task / (HALF_NE * S::NV)) % S::LPK;
+      const int t4 = task / (HALF_NE * S::NV * S::LPK);
       const int j = 32 * uu + P * vv;
       int4* tab = lut + t4 * (S::TBYTES / 16);
-      int a[4];
+      int e[4];
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh)
-        a[hh] = __float2int_rn(qs[4 * t4 + hh][j] * prm.centroid[flo] * hscale[4 * t4 + hh]);
-      if constexpr (P == 1) {
-        tab[slot_of(uu, vv, flo)] = make_int4(a[0], a[1], a[2], a[3]);
-        tab[slot_of(uu, vv, L - 1 - flo)] = make_int4(-a[0], -a[1], -a[2], -a[3]);
-      } else {
-        int bq[4][HL];
-#pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
-#pragma unroll
-          for (int k = 0; k < HL; ++k)
-            bq[hh][k] = __float2int_rn(qs[4 * t4 + hh][j + 1] * prm.centroid[k] *
-                                       hscale[4 * t4 + hh]);
-        }
-#pragma unroll
-        for (int fhi = 0; fhi < L; ++fhi) {
-          int bv[4];
-#pragma unroll
-          for (int hh = 0; hh < 4; ++hh) bv[hh] = fhi < HL ? bq[hh][fhi] : -bq[hh][L - 1 - fhi];
-          tab[slot_of(uu, vv, flo | (fhi << BITS))] =
-              make_int4(a[0] + bv[0], a[1] + bv[1], a[2] + bv[2], a[3] + bv[3]);
-          tab[slot_of(uu, vv, (L - 1 - flo) | (fhi << BITS))] =
-              make_int4(bv[0] - a[0], bv[1] - a[1], bv[2] - a[2], bv[3] - a[3]);
+      for (int hh = 0; hh < 4; ++hh) {
+        const int g = 4 * t4 + hh;
+        const float sc = hscale[g];
+        if constexpr (P == 1) {
+          e[hh] = __float2int_rn(qs[g][j] * cent[f] * sc);
+        } else {
+          e[hh] = __float2int_rn(qs[g][j] * cent[f & (L - 1)] * sc) +
+                  __float2int_rn(qs[g][j + 1] * cent[f >> BITS] * sc);
         }
       }
+      const int fm = (S::NE - 1) ^ f;            // every field mirrored
+      // With four lanes per key, component i of chunk u's entries holds head
+      // u ^ i (see quad_reduce_scatter); otherwise heads are in order.
+      const int pu = S::LPK == 4 ? (uu & 3) : 0;
+      const int c0 = e[0 ^ pu], c1 = e[1 ^ pu], c2 = e[2 ^ pu], c3 = e[3 ^ pu];
+      tab[slot_of(uu, vv, f)] = make_int4(c0, c1, c2, c3);
+      tab[slot_of(uu, vv, fm)] = make_int4(-c0, -c1, -c2, -c3);
     }
   }
 
@@ -318,12 +329,28 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
         256 * (u * S::ROWS_U + (vv / 16) * S::NE) + 16 * ((vv + S::KPG * u) & 15));
   }
   const uint32_t rot = static_cast<uint32_t>(kslot * S::FB);
-  const bool hi1 = (u & 1) != 0, hi2 = (u & 2) != 0;
   const uint32_t fmask = ((1u << S::FB) - 1u) << 8;
+  // Scores of this block's heads through a raw buffer resource (uniform
+  // base: the block's first head row); each lane stores head u (and u + 4)
+  // at a fixed per-lane offset plus a per-batch scalar offset.
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+      scores + (static_cast<size_t>(bi) * prm.Hq + h0) * prm.T, 0,
+      static_cast<int>(static_cast<uint32_t>(nvalid) * static_cast<uint32_t>(prm.T) * 4u),
+      kRsrcWord3);
+  uint32_t vsc[NT];
+  float ginv_u[NT];
+#pragma unroll
+  for (int t4 = 0; t4 < NT; ++t4) {
+    const uint32_t g = static_cast<uint32_t>((4 * t4 + u) % GB);
+    vsc[t4] = (g * static_cast<uint32_t>(prm.T) + static_cast<uint32_t>(tw + kw)) * 4u;
+  }
+  const uint32_t tile_keys = static_cast<uint32_t>(t1 - tw);  // this wave's tokens past tw
   __syncthreads();
-  float ginv[GB];                               // 2^-e per head (this lane's heads)
+  float ginv[GB];                               // 2^-e per head
 #pragma unroll
   for (int g = 0; g < GB; ++g) ginv[g] = hinv[g];
+#pragma unroll
+  for (int t4 = 0; t4 < NT; ++t4) ginv_u[t4] = hinv[(4 * t4 + u) % GB];
 
   // 3. stream the tile, keeping PD batches of records in flight and working
   //    on IL of them at once (independent lookups interleave in the LDS
@@ -373,18 +400,20 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 #pragma unroll
       for (int il = 0; il < IL; ++il) {
         const int64_t t = tb0 + static_cast<int64_t>(pd0 + il) * KPB + kw;
-        const bool valid = t < t1;
+        const uint32_t tb_rel = static_cast<uint32_t>(tb0 - tw) + (pd0 + il) * KPB;
+        const bool valid = tb_rel + kw < tile_keys;
         if constexpr (S::LPK == 4) {
           // lane u of the key ends with head u (and u + 4 when NT = 2)
 #pragma unroll
           for (int t4 = 0; t4 < NT; ++t4) {
             const uint32_t a4[4] = {acc[il][4 * t4], acc[il][4 * t4 + 1], acc[il][4 * t4 + 2],
                                     acc[il][4 * t4 + 3]};
-            const uint32_t tot = quad_reduce_scatter(a4, hi1, hi2);
-            const int g = 4 * t4 + u;
-            if (valid && g < nvalid) {
-              scores[(static_cast<size_t>(bi) * prm.Hq + h0 + g) * prm.T + t] =
-                  nk[il] * (static_cast<float>(static_cast<int32_t>(tot)) * ginv[g]);
+            const uint32_t tot = quad_reduce_scatter(a4);
+            if (valid && 4 * t4 + u < nvalid) {
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  __builtin_bit_cast(uint32_t, nk[il] * (static_cast<float>(
+                                                   static_cast<int32_t>(tot)) * ginv_u[t4])),
+                  rsc, vsc[t4], tb_rel * 4u, 0);
             }
           }
         } else {
