@@ -33,11 +33,11 @@ CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
 # files below); otherwise traffic is reported as null.
 COUNTER_TRAFFIC = {
     "write": {"sources": ["axr_write.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "15188abfe85a0b0666c86a57e7f983f9025d8a6c",
-              "bytes": (262190.2 * 2.0 + 106815.9) * 1024},
+              "sha1": "f4489f91f4cc1797ae273b273e5af3c8a95e57de",
+              "bytes": (262190.8 * 2.0 + 106871.0) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "745673f0709c5c7f587f85ef6a477cdfc7ac23b7",
-              "bytes": (53558.0 * 2.0 + 32775.7) * 1024},
+              "sha1": "8f85d151722ae0b3a4685a5b11365db860bde79d",
+              "bytes": (53551.2 * 2.0 + 32782.6) * 1024},
 }
 
 
