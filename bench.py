@@ -58,8 +58,8 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cold-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -157,6 +157,7 @@ def main():
     # without leaving dirty lines behind.
     log("cold-cache score timing")
     flush = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    flush_bytes = flush.numel() * flush.element_size()
     sink = torch.empty((), dtype=torch.float32, device=dev)
     cold = []
     for _ in range(args.cold_reps):
@@ -169,6 +170,17 @@ def main():
         cold.append(e0.elapsed_time(e1))
     cold.sort()
     cold_ms = cold[len(cold) // 2]
+
+    # Achievable-bandwidth ceilings on this machine (include/axr_probe.h): a
+    # bare 2 GiB read stream, and a stream with the score kernel's traffic
+    # (its read bytes, then its write bytes, per block).
+    log("bandwidth probes")
+    psink = torch.zeros(4, dtype=torch.int32, device=dev)
+    read_ms = per_launch_ms(lambda: axr.probe_read_stream(flush, psink), 10)
+    score_in = n * (d * b // 8 + 4)
+    score_out = n * 4 * (Hq // Hkv)
+    shaped_ms = per_launch_ms(lambda: axr.probe_read_write(keys, score_in, scores, score_out),
+                              args.steps)
     del flush, sink
 
     write_bytes_per_key = d * keys.element_size() + d * b // 8 + 4
@@ -203,6 +215,13 @@ def main():
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic(dominant),
                      "bytes_per_launch": dom_bytes},
+        "ceiling": {
+            "read_stream_GB_per_s": flush_bytes / (read_ms * 1e-3) / 1e9,
+            "read_stream_bytes": flush_bytes,
+            "score_shaped_stream_GB_per_s": (score_in + score_out) / (shaped_ms * 1e-3) / 1e9,
+            "score_shaped_stream_ms": shaped_ms,
+            "score_frac_of_shaped_stream": shaped_ms / score_ms,
+        },
         "kernels": {
             "write": {"ms": write_ms, "keys_per_s": n / (write_ms * 1e-3),
                       "GB_per_s": write_gbs, "frac_hbm": write_gbs / HBM_PEAK_GBS,

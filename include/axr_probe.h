@@ -1,0 +1,38 @@
+/*
+ * axr_probe.h -- bandwidth probes shipped with libaxr for measurement.
+ *
+ * Not part of the method: plain streaming kernels that report the HBM rate a
+ * bare stream reaches on the running machine, so that the scoring and
+ * quantization kernels can be quoted against it as well as against the
+ * published peak.  Both calls validate their arguments before any HIP call,
+ * enqueue one kernel on `stream` (a hipStream_t cast to void*, NULL = default
+ * stream), never synchronise and allocate nothing.  Return 0 on success, -1 on
+ * a bad argument, -4 when the launch fails.
+ */
+#ifndef AXR_PROBE_H
+#define AXR_PROBE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Reads `bytes` bytes of device memory at `buf` (16-byte aligned, bytes a
+ * multiple of 16) with 16-byte loads.  `sink` is a device uint32 that the
+ * kernel writes only in a case that cannot occur for real data; it keeps the
+ * loads from being optimised away. */
+int axr_probe_read_stream(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
+/* Reads `in_bytes` bytes at `in` (16-byte aligned, multiple of 16) and writes
+ * `out_bytes` bytes at `out` (4-byte aligned, multiple of 4); every block
+ * reads a contiguous share of the input and then writes a contiguous share of
+ * the output. */
+int axr_probe_read_write(const void* in, int64_t in_bytes, void* out, int64_t out_bytes,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AXR_PROBE_H */

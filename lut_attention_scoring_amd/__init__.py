@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "AxrError", "LIB_PATH", "lib", "version", "codebook", "sign_words",
-    "packed_words", "quantize_keys", "score", "transform",
+    "packed_words", "quantize_keys", "score", "transform", "probe_read_stream",
+    "probe_read_write",
     "F32", "F16", "BF16",
 ]
 
@@ -42,7 +43,7 @@ class AxrError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing; build it with `python -m lut_attention_scoring_amd.build`")
+            f"{LIB_PATH} is missing; build it with `python lut_attention_scoring_amd/build.py`")
     so = ctypes.CDLL(LIB_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     dp = ctypes.POINTER(ctypes.c_double)
@@ -59,6 +60,10 @@ def _load():
     so.axr_score.argtypes = [vp, i32, vp, vp, u32p, i32, i32, i32, i64, i64, i32, i32, vp, vp]
     so.axr_transform.restype = i32
     so.axr_transform.argtypes = [vp, i32, i64, i32, u32p, i32, vp, vp]
+    so.axr_probe_read_stream.restype = i32
+    so.axr_probe_read_stream.argtypes = [vp, i64, vp, vp]
+    so.axr_probe_read_write.restype = i32
+    so.axr_probe_read_write.argtypes = [vp, i64, vp, i64, vp]
     return so
 
 
@@ -170,3 +175,22 @@ def transform(x: torch.Tensor, sign_bits, normalize: bool = True, out: torch.Ten
     _check(lib.axr_transform(x.data_ptr(), _dtype_code(x), n, d, wp, int(bool(normalize)),
                              out.data_ptr(), _stream(x)))
     return out
+
+
+def probe_read_stream(buf: torch.Tensor, sink: torch.Tensor, nbytes: int = None):
+    """Bandwidth probe (include/axr_probe.h): stream-read `nbytes` of `buf`."""
+    _need_cuda(buf, sink)
+    nbytes = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    if lib.axr_probe_read_stream(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(buf)) != 0:
+        raise AxrError(EINVAL, "axr_probe_read_stream rejected its arguments")
+
+
+def probe_read_write(src: torch.Tensor, in_bytes: int, dst: torch.Tensor, out_bytes: int):
+    """Bandwidth probe: read `in_bytes` of `src`, write `out_bytes` of `dst`."""
+    _need_cuda(src, dst)
+    if (in_bytes > src.numel() * src.element_size()
+            or out_bytes > dst.numel() * dst.element_size()):
+        raise ValueError("probe sizes exceed the buffers")
+    if lib.axr_probe_read_write(src.data_ptr(), int(in_bytes), dst.data_ptr(), int(out_bytes),
+                                _stream(src)) != 0:
+        raise AxrError(EINVAL, "axr_probe_read_write rejected its arguments")

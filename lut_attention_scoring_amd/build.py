@@ -1,6 +1,6 @@
 """Builds libaxr.so (HIP kernels for gfx950 + C-ABI host code) in-tree.
 
-Usage: python -m lut_attention_scoring_amd.build   (or build() from Python).
+Usage: python lut_attention_scoring_amd/build.py   (or build() from Python).
 """
 
 import os
@@ -13,7 +13,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libaxr.so")
 
-SOURCES = ["axr_api.cpp", "axr_codebook.cpp", "axr_write.hip", "axr_score.hip"]
+SOURCES = ["axr_api.cpp", "axr_codebook.cpp", "axr_write.hip", "axr_score.hip",
+           "axr_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -199,26 +199,41 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   constexpr int R = D / 64;
   float v[R];
   if (wave < GB) {
-    const int g = wave;
+    // All loads of the head are issued before the first wait (one memory
+    // round trip); the sign words are kernel arguments read at uniform
+    // indices, so they come from scalar registers.
+    const int g = wave < nvalid ? wave : 0;   // padding heads load head 0, zeroed below
+    const size_t qrow = (static_cast<size_t>(bi) * prm.Hq + h0 + g) * D + lane;
+    uint32_t raw[R];
+    if (qdt == AXR_F32) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) raw[r] = static_cast<const uint32_t*>(q)[qrow + 64 * r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) raw[r] = static_cast<const uint16_t*>(q)[qrow + 64 * r];
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int j = lane + 64 * r;
-      float x = 0.0f;
-      if (g < nvalid) {
-        const size_t off = (static_cast<size_t>(bi) * prm.Hq + h0 + g) * D + j;
-        if (qdt == AXR_F32) {
-          x = static_cast<const float*>(q)[off];
-        } else if (qdt == AXR_F16) {
-          x = __half2float(static_cast<const __half*>(q)[off]);
-        } else {
-          x = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(q)[off]) << 16);
-        }
-        if ((prm.sign[j >> 5] >> (j & 31)) & 1u) x = -x;
+      float x;
+      if (qdt == AXR_F32) {
+        x = __uint_as_float(raw[r]);
+      } else if (qdt == AXR_F16) {
+        x = __half2float(__ushort_as_half(static_cast<unsigned short>(raw[r])));
+      } else {
+        x = __uint_as_float(raw[r] << 16);
       }
-      v[r] = x;
+      const uint32_t s_lo = __builtin_amdgcn_readfirstlane(prm.sign[2 * r]);
+      const uint32_t s_hi = __builtin_amdgcn_readfirstlane(prm.sign[2 * r + 1]);
+      const uint32_t sw = (lane & 32) ? s_hi : s_lo;
+      const uint32_t neg = ((sw >> (lane & 31)) & 1u) << 31;
+      v[r] = wave < nvalid ? __uint_as_float(__float_as_uint(x) ^ neg) : 0.0f;
     }
   }
-  if (tid < L) cent[tid] = prm.centroid[tid];
+  if (tid == 0) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) cent[i] = prm.centroid[i];
+  }
+
   if (wave < GB) {
     const int g = wave;
 #pragma unroll
