@@ -33,11 +33,11 @@ CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
 # files below); otherwise traffic is reported as null.
 COUNTER_TRAFFIC = {
     "write": {"sources": ["axr_write.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "f4489f91f4cc1797ae273b273e5af3c8a95e57de",
-              "bytes": (262190.8 * 2.0 + 106871.0) * 1024},
+              "sha1": "0b21968884ccb26af253ee7bbf4f0f70f6d63d73",
+              "bytes": (262385.8 * 2.0 + 107270.5) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "8f85d151722ae0b3a4685a5b11365db860bde79d",
-              "bytes": (53551.2 * 2.0 + 32782.6) * 1024},
+              "sha1": "bdcd5a0c1c87004442c9c3e7a550d30e6271713c",
+              "bytes": (53551.9 * 2.0 + 32793.2) * 1024},
 }
 
 

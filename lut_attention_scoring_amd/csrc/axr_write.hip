@@ -23,7 +23,9 @@
 // over the positive thresholds of the symmetric codebook, then mirrors for
 // z <= 0 (a coordinate equal to +0, and every coordinate of a zero key, takes
 // the cell just below the middle threshold 0, as a value equal to a
-// threshold does).
+// threshold does).  The b index bits of each coordinate are lane masks of
+// compares; they are appended to the record words most significant bit
+// first, one add-with-carry per bit.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -103,52 +105,45 @@ __device__ __forceinline__ void reg_stage(float (&x)[32]) {
   }
 }
 
-// Positive-side cell index minus one: HALF - 1 + #{positive thresholds < a},
-// a = |z|.  (The +1 is added once per packed word; written this way the
-// compare feeds a carry-in add instead of a select.)
+// Bits of one coordinate's index, most significant first.  With
+// p = (z > 0) and a binary search on |z| against the positive thresholds
+// (decisions c_k, most significant first), the positive side has index
+// HALF + cell = (1, c_{b-2}, ..., c_0) and the mirrored negative side
+// HALF - 1 - cell = (0, !c_{b-2}, ..., !c_0): every lower bit is c_k == p.
+// z = +0 and z = -0 take the cell just below the middle threshold (0), as
+// the count of thresholds strictly below z requires, so a zero key needs no
+// special case.
 template <int BITS>
-__device__ __forceinline__ uint32_t positive_cell_m1(float a, const float (&S)[8]) {
-  constexpr uint32_t B = (1u << (BITS - 1)) - 1u;
+__device__ __forceinline__ void index_bits(float z, const float (&S)[8], uint64_t (&bit)[BITS]) {
+  const uint64_t p = __builtin_amdgcn_ballot_w64(z > 0.0f);
+  const float a = fabsf(z);
+  bit[BITS - 1] = p;
   if constexpr (BITS == 2) {
-    return B + (a > S[0] ? 1u : 0u);
+    bit[0] = ~(__builtin_amdgcn_ballot_w64(a > S[0]) ^ p);
   } else if constexpr (BITS == 3) {
     const bool c1 = a > S[1];
-    const float t = c1 ? S[2] : S[0];
-    return (c1 ? B + 2u : B) + (a > t ? 1u : 0u);
+    const bool c0 = a > (c1 ? S[2] : S[0]);
+    bit[1] = ~(__builtin_amdgcn_ballot_w64(c1) ^ p);
+    bit[0] = ~(__builtin_amdgcn_ballot_w64(c0) ^ p);
   } else {
     static_assert(BITS == 4, "b must be 2, 3 or 4");
-    const bool c1 = a > S[3];
-    const float t2 = c1 ? S[5] : S[1];
-    const bool c2 = a > t2;
-    const float t3 = c1 ? (c2 ? S[6] : S[4]) : (c2 ? S[2] : S[0]);
-    return (c1 ? B + 4u : B) + (c2 ? 2u : 0u) + (a > t3 ? 1u : 0u);
+    const bool c2 = a > S[3];
+    const bool c1 = a > (c2 ? S[5] : S[1]);
+    const bool c0 = a > (c2 ? (c1 ? S[6] : S[4]) : (c1 ? S[2] : S[0]));
+    bit[2] = ~(__builtin_amdgcn_ballot_w64(c2) ^ p);
+    bit[1] = ~(__builtin_amdgcn_ballot_w64(c1) ^ p);
+    bit[0] = ~(__builtin_amdgcn_ballot_w64(c0) ^ p);
   }
 }
 
-// Constant with a 1 in the lowest bit of every BITS-bit field that lies
-// wholly inside record word i (the fields of 32 coordinates span BITS words;
-// fields split across two words are excluded).
-template <int BITS>
-__device__ __forceinline__ constexpr uint32_t ones_word(int i) {
-  uint32_t w = 0u;
-  for (int r = 0; r < 32; ++r) {
-    const int pos = r * BITS;
-    if ((pos >> 5) == i && (pos & 31) + BITS <= 32) w |= 1u << (pos & 31);
-  }
-  return w;
-}
-
-// Record word i of a key whose 32 coordinates all take cell HALF - 1.
-template <int BITS>
-__device__ __forceinline__ constexpr uint32_t zero_key_word(int i) {
-  const uint32_t v = (1u << (BITS - 1)) - 1u;
-  uint32_t w = 0u;
-  for (int r = 0; r < 32; ++r) {
-    const int pos = r * BITS;
-    if ((pos >> 5) == i) w |= v << (pos & 31);
-    if ((pos >> 5) + 1 == i && (pos & 31) + BITS > 32) w |= v >> (32 - (pos & 31));
-  }
-  return w;
+// w + w + (this lane's bit of m): appends one bit below w's bits, as one add
+// whose carry-in is the lane mask (the compiler would turn the shift-add
+// into shifts, selects and ors).
+__device__ __forceinline__ uint32_t append_bit(uint32_t w, uint64_t m) {
+  uint32_t r;
+  uint64_t carry_out;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(w), "s"(m));
+  return r;
 }
 
 template <int DT>
@@ -268,43 +263,22 @@ __global__ __launch_bounds__(kBlock) void write_kernel(const void* __restrict__ 
       float S[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) S[i] = P[i] * nrm;
-      // words = (P + ONES) ^ N: P holds the positive-side cells minus one,
-      // ONES adds 1 to every field inside a word (no carries: a positive-side
-      // cell fits its field), N flips all bits of the fields whose coordinate
-      // is <= 0 (mirror to the negative side).
-      constexpr uint32_t FLIP = (1u << BITS) - 1u;
-      uint32_t Pw[BITS], Nw[BITS];
-#pragma unroll
-      for (int i = 0; i < BITS; ++i) Pw[i] = Nw[i] = 0u;
-#pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        const uint32_t mm = positive_cell_m1<BITS>(fabsf(x[r]), S);
-        // all ones when z <= 0: the sign of the signed integer bits(z) - 1
-        // (+0 -> -1, positives -> >= 0, negatives -> < 0).  Only -0 reads as
-        // positive; it arises from zero inputs, and a zero key is handled
-        // below.
-        const uint32_t nm = static_cast<uint32_t>(
-            static_cast<int32_t>(__float_as_uint(x[r]) - 1u) >> 31);
-        const int pos = r * BITS, wi = pos >> 5, sh = pos & 31;
-        if (sh + BITS <= 32) {
-          Pw[wi] |= mm << sh;
-          Nw[wi] |= nm & (FLIP << sh);
-        } else {
-          // a field split across two words gets its +1 here (a carry out of
-          // the lower word would be lost)
-          const uint32_t m1 = mm + 1u;
-          Pw[wi] |= m1 << sh;
-          Nw[wi] |= nm & (FLIP << sh);
-          Pw[wi + 1] |= m1 >> (32 - sh);
-          Nw[wi + 1] |= nm & (FLIP >> (32 - sh));
-        }
-      }
-      // A zero key has z = +-0 everywhere: every coordinate sits on the middle
-      // threshold and takes the cell below it (HALF - 1 in every field).
+      // Record words filled most significant bit first: walking the bit
+      // positions downwards, each index bit is appended to its word as
+      // w + w + bit (one add with carry-in).
       uint32_t words[BITS];
 #pragma unroll
-      for (int i = 0; i < BITS; ++i)
-        words[i] = nrm > 0.0f ? (Pw[i] + ones_word<BITS>(i)) ^ Nw[i] : zero_key_word<BITS>(i);
+      for (int i = 0; i < BITS; ++i) words[i] = 0u;
+#pragma unroll
+      for (int r = 31; r >= 0; --r) {
+        uint64_t bit[BITS];                     // lane masks
+        index_bits<BITS>(x[r], S, bit);
+#pragma unroll
+        for (int k = BITS - 1; k >= 0; --k) {
+          const int wi = (r * BITS + k) >> 5;
+          words[wi] = append_bit(words[wi], bit[k]);
+        }
+      }
       if (valid) {
         uint32_t* dst = packed + static_cast<size_t>(key) * W + u * BITS;
         if constexpr (BITS == 2) {
