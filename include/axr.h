@@ -115,6 +115,39 @@ int axr_score(const void* q, int q_dtype, const uint32_t* packed, const float* n
               int d, int b, float* scores, void* stream);
 
 /*
+ * Decode-step write (AXELRAM, Abstract: each key is quantized once, when it is
+ * written).  Quantizes one new key per (sequence, KV head) exactly as
+ * axr_quantize_keys does and stores its record and norm in a cache laid out
+ * [B][Hkv][t_cap] (records of W words, as above):
+ *   key (bi, h) -> packed row (bi*Hkv + h)*t_cap + pos[bi], norms likewise.
+ *   keys   : device, [B][Hkv][d] of `dtype`, 16-byte aligned
+ *   pos    : device int32 [B], the slot of each sequence's new token; a
+ *            sequence whose pos lies outside [0, t_cap) is skipped (nothing
+ *            is written for it)
+ *   packed : device uint32 [B][Hkv][t_cap][W], 16-byte aligned (in/out: only
+ *            the appended slots are written)
+ *   norms  : device float [B][Hkv][t_cap], 4-byte aligned (in/out)
+ * B = 0 or Hkv = 0 is a no-op.  Requires t_cap >= 1 and B*Hkv < 2^31.
+ * Errors: AXR_EINVAL, AXR_EUNSUPPORTED, AXR_EALIGN, AXR_EHIP.
+ */
+int axr_append_keys(const void* keys, int dtype, int B, int Hkv, int d, int b,
+                    const uint32_t* sign_bits, const int32_t* pos, int64_t t_cap,
+                    uint32_t* packed, float* norms, void* stream);
+
+/*
+ * Read path over sequences of different lengths (AXELRAM, Abstract: table
+ * lookup on read).  As axr_score, but batch row bi scores only tokens
+ * t < min(max(lens[bi], 0), T); scores[bi][h][t] for later t are not written.
+ *   lens : device int32 [B], 4-byte aligned
+ *   T    : row length of `scores` ([B][Hq][T]) and the largest length scored
+ * Same requirements and errors as axr_score (lens must be non-null when B > 0
+ * and T > 0).
+ */
+int axr_score_ragged(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
+                     const uint32_t* sign_bits, int B, int Hq, int Hkv, const int32_t* lens,
+                     int64_t T, int64_t t_cap, int d, int b, float* scores, void* stream);
+
+/*
  * Diagnostic export of the write-path transform (the same device code the
  * quantizer runs): y[i] = H_d (s * x[i]) / sqrt(d), divided by ||x[i]|| when
  * normalize != 0 (y = 0 for a zero row).

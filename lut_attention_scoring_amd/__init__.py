@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "AxrError", "LIB_PATH", "lib", "version", "codebook", "sign_words",
-    "packed_words", "quantize_keys", "score", "transform", "probe_read_stream",
+    "packed_words", "quantize_keys", "append_keys", "score", "transform", "probe_read_stream",
     "probe_read_write",
     "F32", "F16", "BF16",
 ]
@@ -58,6 +58,12 @@ def _load():
     so.axr_quantize_keys.argtypes = [vp, i32, i64, i32, i32, u32p, vp, vp, vp]
     so.axr_score.restype = i32
     so.axr_score.argtypes = [vp, i32, vp, vp, u32p, i32, i32, i32, i64, i64, i32, i32, vp, vp]
+    i32p = ctypes.c_void_p
+    so.axr_append_keys.restype = i32
+    so.axr_append_keys.argtypes = [vp, i32, i32, i32, i32, i32, u32p, i32p, i64, vp, vp, vp]
+    so.axr_score_ragged.restype = i32
+    so.axr_score_ragged.argtypes = [vp, i32, vp, vp, u32p, i32, i32, i32, i32p, i64, i64, i32,
+                                    i32, vp, vp]
     so.axr_transform.restype = i32
     so.axr_transform.argtypes = [vp, i32, i64, i32, u32p, i32, vp, vp]
     so.axr_probe_read_stream.restype = i32
@@ -144,10 +150,31 @@ def quantize_keys(keys: torch.Tensor, sign_bits, b: int, packed: torch.Tensor = 
     return packed, norms
 
 
+def append_keys(keys: torch.Tensor, sign_bits, b: int, packed: torch.Tensor,
+                norms: torch.Tensor, pos: torch.Tensor):
+    """Decode-step write: keys [B, Hkv, d] quantized into slot pos[bi] (int32
+    device tensor [B]) of the cache packed [B, Hkv, t_cap, W], norms
+    [B, Hkv, t_cap].  Sequences whose pos is outside [0, t_cap) are skipped."""
+    B, Hkv, d = keys.shape
+    Bc, Hc, t_cap, W = packed.shape
+    if (Bc, Hc) != (B, Hkv) or W != packed_words(d, b) or tuple(norms.shape) != (B, Hkv, t_cap):
+        raise ValueError("keys, packed and norms shapes disagree")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (B,):
+        raise ValueError("pos must be an int32 tensor of shape [B]")
+    _need_cuda(keys, packed, norms, pos)
+    words, wp = _words_ptr(sign_words(sign_bits))
+    _check(lib.axr_append_keys(keys.data_ptr(), _dtype_code(keys), B, Hkv, d, b, wp,
+                               pos.data_ptr(), t_cap, packed.data_ptr(), norms.data_ptr(),
+                               _stream(keys)))
+    return packed, norms
+
+
 def score(q: torch.Tensor, packed: torch.Tensor, norms: torch.Tensor, sign_bits, b: int,
-          T: int = None, out: torch.Tensor = None):
+          T: int = None, out: torch.Tensor = None, lens: torch.Tensor = None):
     """Read path: q [B, Hq, d], packed [B, Hkv, t_cap, W], norms [B, Hkv, t_cap]
-    -> scores fp32 [B, Hq, T] (T defaults to t_cap)."""
+    -> scores fp32 [B, Hq, T] (T defaults to t_cap).  With `lens` (int32
+    device tensor [B]) row bi is scored only for t < lens[bi]; later entries
+    of `out` are left as they were."""
     B, Hq, d = q.shape
     Bk, Hkv, t_cap, W = packed.shape
     if Bk != B or W != packed_words(d, b) or tuple(norms.shape) != (B, Hkv, t_cap):
@@ -159,8 +186,16 @@ def score(q: torch.Tensor, packed: torch.Tensor, norms: torch.Tensor, sign_bits,
     if tuple(out.shape) != (B, Hq, T):
         raise ValueError("out has the wrong shape")
     words, wp = _words_ptr(sign_words(sign_bits))
-    _check(lib.axr_score(q.data_ptr(), _dtype_code(q), packed.data_ptr(), norms.data_ptr(), wp,
-                         B, Hq, Hkv, T, t_cap, d, b, out.data_ptr(), _stream(q)))
+    if lens is None:
+        _check(lib.axr_score(q.data_ptr(), _dtype_code(q), packed.data_ptr(), norms.data_ptr(),
+                             wp, B, Hq, Hkv, T, t_cap, d, b, out.data_ptr(), _stream(q)))
+    else:
+        if lens.dtype != torch.int32 or tuple(lens.shape) != (B,):
+            raise ValueError("lens must be an int32 tensor of shape [B]")
+        _need_cuda(lens)
+        _check(lib.axr_score_ragged(q.data_ptr(), _dtype_code(q), packed.data_ptr(),
+                                    norms.data_ptr(), wp, B, Hq, Hkv, lens.data_ptr(), T, t_cap,
+                                    d, b, out.data_ptr(), _stream(q)))
     return out
 
 

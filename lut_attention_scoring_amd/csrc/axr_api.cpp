@@ -78,7 +78,8 @@ int axr_codebook(int d, int b, double* centroids, double* thresholds) {
 
 static int write_common(const void* x, int dtype, int64_t n, int d, int b,
                         const uint32_t* sign_bits, uint32_t* packed, float* norms, float* y,
-                        int mode, void* stream) {
+                        int mode, void* stream, const int32_t* pos = nullptr,
+                        int64_t t_cap = 0, int Hkv = 1) {
   int rc = check_common(d, b, dtype, sign_bits);
   if (rc != AXR_OK) return rc;
   if (n < 0) return fail(AXR_EINVAL, "n=%lld is negative", static_cast<long long>(n));
@@ -102,6 +103,9 @@ static int write_common(const void* x, int dtype, int64_t n, int d, int b,
   const double sqrt_d = std::sqrt(static_cast<double>(d));
   for (int i = 0; i + 1 < half; ++i) p.tpos[i] = static_cast<float>(cb.threshold[half + i] * sqrt_d);
   p.inv_sqrt_d = static_cast<float>(1.0 / sqrt_d);
+  p.pos = pos;
+  p.t_cap = t_cap;
+  p.Hkv = Hkv;
   int err = axr::launch_write(x, dtype, n, d, b, p, packed, norms, y, mode, stream);
   return hip_status(err, "write kernel launch");
 }
@@ -119,9 +123,23 @@ int axr_transform(const void* x, int dtype, int64_t n, int d, const uint32_t* si
                       normalize ? axr::kWriteTransformNormalized : axr::kWriteTransform, stream);
 }
 
-int axr_score(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
-              const uint32_t* sign_bits, int B, int Hq, int Hkv, int64_t T, int64_t t_cap,
-              int d, int b, float* scores, void* stream) {
+int axr_append_keys(const void* keys, int dtype, int B, int Hkv, int d, int b,
+                    const uint32_t* sign_bits, const int32_t* pos, int64_t t_cap,
+                    uint32_t* packed, float* norms, void* stream) {
+  if (B < 0 || Hkv < 0) return fail(AXR_EINVAL, "negative size (B=%d Hkv=%d)", B, Hkv);
+  if (t_cap < 1) return fail(AXR_EINVAL, "t_cap=%lld must be >= 1", static_cast<long long>(t_cap));
+  const int64_t n = static_cast<int64_t>(B) * Hkv;
+  if (n > INT32_MAX) return fail(AXR_EUNSUPPORTED, "B*Hkv=%lld exceeds 2^31-1",
+                                 static_cast<long long>(n));
+  if (n > 0 && pos == nullptr) return fail(AXR_EINVAL, "pos is null");
+  if (n > 0 && !aligned(pos, 4)) return fail(AXR_EALIGN, "pos must be 4-byte aligned");
+  return write_common(keys, dtype, n, d, b, sign_bits, packed, norms, nullptr,
+                      axr::kWriteQuantize, stream, pos, t_cap, Hkv > 0 ? Hkv : 1);
+}
+
+static int score_common(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
+                        const uint32_t* sign_bits, int B, int Hq, int Hkv, const int32_t* lens,
+                        int64_t T, int64_t t_cap, int d, int b, float* scores, void* stream) {
   int rc = check_common(d, b, q_dtype, sign_bits);
   if (rc != AXR_OK) return rc;
   if (B < 0 || Hq < 0 || Hkv < 0 || T < 0)
@@ -154,8 +172,27 @@ int axr_score(const void* q, int q_dtype, const uint32_t* packed, const float* n
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.G = G;
+  p.lens = lens;
   int err = axr::launch_score(q, q_dtype, packed, norms, B, d, b, p, scores, stream);
   return hip_status(err, "score kernel launch");
+}
+
+int axr_score(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
+              const uint32_t* sign_bits, int B, int Hq, int Hkv, int64_t T, int64_t t_cap,
+              int d, int b, float* scores, void* stream) {
+  return score_common(q, q_dtype, packed, norms, sign_bits, B, Hq, Hkv, nullptr, T, t_cap, d, b,
+                      scores, stream);
+}
+
+int axr_score_ragged(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
+                     const uint32_t* sign_bits, int B, int Hq, int Hkv, const int32_t* lens,
+                     int64_t T, int64_t t_cap, int d, int b, float* scores, void* stream) {
+  if (B > 0 && T > 0) {
+    if (lens == nullptr) return fail(AXR_EINVAL, "lens is null");
+    if (!aligned(lens, 4)) return fail(AXR_EALIGN, "lens must be 4-byte aligned");
+  }
+  return score_common(q, q_dtype, packed, norms, sign_bits, B, Hq, Hkv, lens, T, t_cap, d, b,
+                      scores, stream);
 }
 
 }  // extern "C"

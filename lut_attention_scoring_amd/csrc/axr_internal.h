@@ -1,5 +1,6 @@
 // Internal interfaces between the C-ABI layer (axr_api.cpp), the host
-// codebook solver (axr_codebook.cpp) and the HIP kernels (axr_kernels.hip).
+// codebook solver (axr_codebook.cpp) and the HIP kernels (axr_write.hip,
+// axr_score.hip).
 #pragma once
 
 #include <stdint.h>
@@ -28,6 +29,11 @@ struct WriteParams {
   uint32_t sign[kMaxSignWords];   // sign bits, word j/32 bit j%32
   float tpos[kMaxLevels / 2];     // positive thresholds times sqrt(d), ascending
   float inv_sqrt_d;
+  // Append mode (pos != nullptr): key i = bi * Hkv + h is stored at cache row
+  // i * t_cap + pos[bi]; keys whose pos lies outside [0, t_cap) are skipped.
+  const int32_t* pos;
+  int64_t t_cap;
+  int Hkv;
 };
 
 struct ScoreParams {
@@ -40,6 +46,7 @@ struct ScoreParams {
   int head_groups;                // G / heads_per_block
   int tiles;                      // token tiles per row
   int64_t tile_len;               // tokens per tile
+  const int32_t* lens;            // optional device [B]: tokens scored per batch row (<= T)
 };
 
 // Launchers (return a hipError_t value as int; 0 = success).

@@ -173,8 +173,15 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   const int kw = lane / S::LPK;                 // key index in the wave
   constexpr int KPB = (NTHREADS / 64) * S::KPW;  // keys per block iteration
   constexpr uint32_t REC_BYTES = S::W * 4;
+  // tokens [0, len) of this batch row are scored: T, or lens[bi] (clamped)
+  int64_t len = prm.T;
+  if (prm.lens != nullptr) {
+    const int64_t l = prm.lens[bi];
+    len = l < 0 ? 0 : (l < prm.T ? l : prm.T);
+  }
   const int64_t t0 = static_cast<int64_t>(tile) * prm.tile_len;
-  const int64_t t1 = (t0 + prm.tile_len < prm.T) ? t0 + prm.tile_len : prm.T;
+  if (t0 >= len) return;                        // block-uniform: nothing to score
+  const int64_t t1 = (t0 + prm.tile_len < len) ? t0 + prm.tile_len : len;
   const size_t rowbase = static_cast<size_t>(row) * prm.t_cap;
 
   // Records and norms of this (batch, KV head) row through raw buffer

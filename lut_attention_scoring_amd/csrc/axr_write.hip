@@ -279,8 +279,16 @@ __global__ __launch_bounds__(kBlock) void write_kernel(const void* __restrict__ 
           words[wi] = append_bit(words[wi], bit[k]);
         }
       }
-      if (valid) {
-        uint32_t* dst = packed + static_cast<size_t>(key) * W + u * BITS;
+      // destination row: the key's own index, or its cache slot when appending
+      int64_t row = key;
+      bool store = valid;
+      if (prm.pos != nullptr && valid) {
+        const int32_t slot = prm.pos[static_cast<uint32_t>(key) / static_cast<uint32_t>(prm.Hkv)];
+        store = slot >= 0 && slot < prm.t_cap;
+        row = key * prm.t_cap + slot;
+      }
+      if (store) {
+        uint32_t* dst = packed + static_cast<size_t>(row) * W + u * BITS;
         if constexpr (BITS == 2) {
           *reinterpret_cast<uint2*>(dst) = make_uint2(words[0], words[1]);
         } else if constexpr (BITS == 4) {
@@ -289,7 +297,7 @@ __global__ __launch_bounds__(kBlock) void write_kernel(const void* __restrict__ 
 #pragma unroll
           for (int i = 0; i < BITS; ++i) dst[i] = words[i];
         }
-        if (u == 0) norms[key] = nrm;
+        if (u == 0) norms[row] = nrm;
       }
     } else {
       float scale = prm.inv_sqrt_d;

@@ -63,6 +63,8 @@ __all__ = [
     "read_path",
     "dequantize_then_dot",
     "multiplications_per_query",
+    "append_keys",
+    "read_path_ragged",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -312,6 +314,36 @@ def read_path(q, packed, norms, signs, b: int):
     idx = unpack_indices(packed, d, b)
     qprime = transform_queries(q, signs)
     return lut_scores(qprime, idx, norms, centroids)
+
+
+def append_keys(packed, norms, keys, pos, signs, b: int):
+    """Decode-step write.  Each key is quantized once, when it is written
+    (AXELRAM, Abstract): key (bi, h) of keys [B, Hkv, d] goes through
+    write_path and its record and norm are stored at slot pos[bi] of the cache
+    packed [B, Hkv, t_cap, W], norms [B, Hkv, t_cap].  A sequence whose slot
+    lies outside [0, t_cap) is left as it was.  Returns new arrays."""
+    out_p = np.array(packed, dtype=np.uint32, copy=True)
+    out_n = np.array(norms, dtype=np.float64, copy=True)
+    new = write_path(keys, signs, b)
+    t_cap = out_p.shape[2]
+    for bi, slot in enumerate(np.asarray(pos).tolist()):
+        if 0 <= slot < t_cap:
+            out_p[bi, :, slot] = new["packed"][bi]
+            out_n[bi, :, slot] = new["norms"][bi]
+    return out_p, out_n
+
+
+def read_path_ragged(q, packed, norms, signs, b: int, lens, T: int):
+    """read_path for sequences of different lengths: row bi is scored for
+    t < min(max(lens[bi], 0), T) and holds NaN elsewhere.  A key's score does
+    not depend on the other keys, so this is read_path restricted to each
+    row's tokens."""
+    full = read_path(q, np.asarray(packed)[:, :, :T], np.asarray(norms)[:, :, :T], signs, b)
+    out = np.full(full.shape, np.nan)
+    for bi, length in enumerate(np.asarray(lens).tolist()):
+        n_tok = min(max(int(length), 0), T)
+        out[bi, :, :n_tok] = full[bi, :, :n_tok]
+    return out
 
 
 def dequantize_then_dot(q, idx, norms, signs, centroids) -> np.ndarray:

@@ -118,3 +118,23 @@ def test_wrong_gqa_mapping_is_caught(monkeypatch):
     monkeypatch.setattr(A, "lut_scores", interleaved)
     sc = A.read_path(q, w["packed"], w["norms"], s, b)
     assert not np.all(sc[:, 2:] == 0.0)
+
+
+def test_append_into_the_next_slot_is_caught(monkeypatch):
+    # mistake: the new key lands one slot after its position
+    from tests import test_oracle_decode as D
+    orig = A.append_keys
+    monkeypatch.setattr(A, "append_keys",
+                        lambda p, n, k, pos, s, b: orig(p, n, k, np.asarray(pos) + 1, s, b))
+    with pytest.raises(AssertionError):
+        D.test_append_token_by_token_equals_bulk_write(3)
+
+
+def test_ragged_length_off_by_one_is_caught(monkeypatch):
+    # mistake: each row scores one token more than its length
+    from tests import test_oracle_decode as D
+    orig = A.read_path_ragged
+    monkeypatch.setattr(A, "read_path_ragged",
+                        lambda q, p, n, s, b, lens, T: orig(q, p, n, s, b, np.asarray(lens) + 1, T))
+    with pytest.raises(AssertionError):
+        D.test_read_path_ragged_is_read_path_on_each_prefix()
