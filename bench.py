@@ -152,6 +152,26 @@ def main():
                              args.steps)
     score_ms = per_launch_ms(lambda: axr.score(q, packed, norms, bits, b, out=scores), args.steps)
 
+    # Decode step on the same cache: one new key per (sequence, KV head)
+    # appended at the last slot, then every sequence scored up to it.
+    log("decode-step timing")
+    import numpy as np
+    rng = np.random.default_rng(105)
+    new_k = torch.from_numpy(rng.standard_normal((B, Hkv, d)).astype(np.float32)).to(
+        keys.dtype).to(dev)
+    pos = torch.full((B,), T - 1, dtype=torch.int32, device=dev)
+    lens = pos + 1
+
+    def append():
+        axr.append_keys(new_k, bits, b, packed, norms, pos)
+
+    def decode_step():
+        append()
+        axr.score(q, packed, norms, bits, b, out=scores, lens=lens)
+
+    append_ms = per_launch_ms(append, args.steps)
+    decode_ms = per_launch_ms(decode_step, args.steps)
+
     # Score kernel alone on a cold cache: read 2 GiB between launches, which
     # evicts the 136 MiB working set from the 256 MB Infinity Cache and L2
     # without leaving dirty lines behind.
@@ -233,6 +253,9 @@ def main():
                       "traffic": counter_traffic("score")},
             "score_cold_cache": {"ms_median": cold_ms, "keys_per_s": n / (cold_ms * 1e-3),
                                  "GB_per_s": cold_gbs, "frac_hbm": cold_gbs / HBM_PEAK_GBS},
+            "decode_step": {"ms": decode_ms, "append_ms": append_ms,
+                            "appended_keys": B * Hkv, "scored_keys": n,
+                            "note": "append one key per (sequence, KV head) + ragged score"},
         },
     }
     if not args.no_cpu_baseline:

@@ -142,3 +142,52 @@ def test_score_rejects_rows_beyond_32bit_offsets():
     # 2^31 bytes of d=128, b=3 records is 44.7M tokens per row
     st, msg = _s(T=45_000_000, t_cap=45_000_000)
     assert st == axr.EUNSUPPORTED and "2 GiB" in msg
+
+
+def _a(keys=FAKE, dtype=axr.F16, B=2, Hkv=4, d=128, b=3, signs=SIGNS, pos=FAKE, t_cap=64,
+       packed=FAKE, norms=FAKE):
+    return _status(axr.lib.axr_append_keys, keys, dtype, B, Hkv, d, b, signs, pos, t_cap, packed,
+                   norms, None)
+
+
+def test_append_validation():
+    assert _a(d=48)[0] == axr.EUNSUPPORTED
+    assert _a(b=1)[0] == axr.EUNSUPPORTED
+    assert _a(dtype=7)[0] == axr.EUNSUPPORTED
+    assert _a(B=-1)[0] == axr.EINVAL
+    assert _a(Hkv=-2)[0] == axr.EINVAL
+    assert _a(t_cap=0)[0] == axr.EINVAL
+    assert _a(pos=None)[0] == axr.EINVAL
+    assert _a(keys=None)[0] == axr.EINVAL
+    assert _a(packed=None)[0] == axr.EINVAL
+    assert _a(norms=None)[0] == axr.EINVAL
+    assert _a(signs=None)[0] == axr.EINVAL
+    assert _a(pos=FAKE + 2)[0] == axr.EALIGN
+    assert _a(keys=FAKE + 4)[0] == axr.EALIGN
+    assert _a(packed=FAKE + 8)[0] == axr.EALIGN
+    st, msg = _a(B=65536, Hkv=65536)
+    assert st == axr.EUNSUPPORTED and "2^31" in msg
+    # nothing to append: no-op with null buffers
+    assert _a(B=0, keys=None, pos=None, packed=None, norms=None)[0] == axr.OK
+    assert _a(Hkv=0, keys=None, pos=None, packed=None, norms=None)[0] == axr.OK
+
+
+def _r(lens=FAKE, **kw):
+    args = dict(q=FAKE, qdt=axr.F16, packed=FAKE, norms=FAKE, signs=SIGNS, B=2, Hq=8, Hkv=2,
+                T=64, t_cap=64, d=128, b=3, scores=FAKE)
+    args.update(kw)
+    a = args
+    return _status(axr.lib.axr_score_ragged, a["q"], a["qdt"], a["packed"], a["norms"],
+                   a["signs"], a["B"], a["Hq"], a["Hkv"], lens, a["T"], a["t_cap"], a["d"],
+                   a["b"], a["scores"], None)
+
+
+def test_score_ragged_validation():
+    assert _r(lens=None)[0] == axr.EINVAL
+    assert _r(lens=FAKE + 2)[0] == axr.EALIGN
+    assert _r(Hq=6, Hkv=4)[0] == axr.EINVAL
+    assert _r(t_cap=10, T=11)[0] == axr.EINVAL
+    assert _r(b=9)[0] == axr.EUNSUPPORTED
+    assert _r(q=None)[0] == axr.EINVAL
+    assert _r(lens=None, B=0, q=None, packed=None, norms=None, scores=None)[0] == axr.OK
+    assert _r(lens=None, T=0, t_cap=0, q=None, packed=None, norms=None, scores=None)[0] == axr.OK

@@ -1,0 +1,237 @@
+"""GPU parity of the decode step ("AXELRAM: Quantize Once, Never Dequantize",
+Abstract: a key is quantized once, when it is written, and read by table
+lookup).  axr_append_keys writes one new key per (sequence, KV head) into its
+cache slot; axr_score_ragged scores every sequence over its own length.  Both
+are compared with the oracle: indices by the boundary rule, scores given the
+GPU's own indices, and every slot or score that must not change is checked
+bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import axelram as A
+from tests._parity import f64, words_u32, assert_indices, assert_scores, assert_norms
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SENTINEL = 12345.5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import lut_attention_scoring_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+
+
+def axr():
+    import lut_attention_scoring_amd as m
+    return m
+
+
+def _keys(rng, shape, dtype, scale=2.0):
+    return torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32)).to(dtype)
+
+
+def _check_appended(new_cpu, packed_after, norms_after, pos, bits, b, label):
+    """Records and norms at the appended slots against the oracle's write of
+    the new keys [B, Hkv, d]."""
+    d = new_cpu.shape[-1]
+    t_cap = packed_after.shape[2]
+    s = A.signs_from_bits(bits)
+    _, t = A.lloyd_max_codebook(d, b)
+    y, onorm = A.transform_keys(f64(new_cpu), s)
+    oidx = A.quantize(y, t)
+    pw = words_u32(packed_after)
+    pn = f64(norms_after)
+    n_checked = 0
+    for bi, slot in enumerate(pos):
+        if 0 <= slot < t_cap:
+            gidx = A.unpack_indices(pw[bi, :, slot], d, b)
+            assert_indices(gidx, oidx[bi], y[bi], t, f"{label} bi={bi}")
+            assert_norms(pn[bi, :, slot], onorm[bi], f"{label} bi={bi}")
+            n_checked += 1
+    return n_checked
+
+
+def _untouched(before_p, before_n, after_p, after_n, pos):
+    """Every slot other than the appended ones is bit-identical."""
+    t_cap = before_p.shape[2]
+    keep = np.ones(before_p.shape[:3], dtype=bool)
+    for bi, slot in enumerate(pos):
+        if 0 <= slot < t_cap:
+            keep[bi, :, slot] = False
+    assert np.array_equal(before_p[keep], after_p[keep])
+    assert np.array_equal(before_n[keep].view(np.uint32), after_n[keep].view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("b", [2, 3, 4])
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_append_into_slots(d, b, dtype):
+    m = axr()
+    rng = np.random.default_rng(1000 + 10 * d + b)
+    B, Hkv, t_cap = 6, 3, 150
+    bits = W.sign_bits(d)
+    cache = _keys(rng, (B, Hkv, t_cap, d), dtype)
+    packed, norms = m.quantize_keys(cache.to(DEV), bits, b)
+    new = _keys(rng, (B, Hkv, d), dtype, scale=5.0)
+    pos = [0, t_cap - 1, 57, -1, t_cap, 2]               # two slots outside [0, t_cap)
+    torch.cuda.synchronize()
+    before_p, before_n = words_u32(packed).copy(), norms.cpu().numpy().copy()
+    m.append_keys(new.to(DEV), bits, b, packed, norms,
+                  torch.tensor(pos, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    after_p, after_n = words_u32(packed), norms.cpu().numpy()
+    assert _check_appended(new, packed, norms, pos, bits, b, f"append d={d} b={b}") == 4
+    _untouched(before_p, before_n, after_p, after_n, pos)
+
+
+def test_append_zero_key_and_exact_ties():
+    # a zero key takes the cell below 0 everywhere; its norm is 0
+    m = axr()
+    d, b, B, Hkv, t_cap = 128, 3, 2, 2, 8
+    bits = W.sign_bits(d)
+    packed = torch.zeros(B, Hkv, t_cap, d * b // 32, dtype=torch.int32, device=DEV)
+    norms = torch.full((B, Hkv, t_cap), -1.0, device=DEV)
+    new = torch.zeros(B, Hkv, d, dtype=torch.float16)
+    new[1, 1, 3] = 1.0                                   # one basis key
+    pos = [5, 0]
+    m.append_keys(new.to(DEV), bits, b, packed, norms,
+                  torch.tensor(pos, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    idx = A.unpack_indices(words_u32(packed[0, :, 5]), d, b)
+    assert np.all(idx == (1 << (b - 1)) - 1)
+    assert np.all(norms[0, :, 5].cpu().numpy() == 0.0)
+    _check_appended(new, packed, norms, pos, bits, b, "zero/basis keys")
+
+
+@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_score_ragged_lengths(G, b):
+    m = axr()
+    rng = np.random.default_rng(2000 + 10 * G + b)
+    d, Hkv, t_cap, T = 128, 2, 1500, 1400
+    lens = [0, 1, 777, T, 5000, -5, 255, 256]             # empty, single, tile edges, clamps
+    B = len(lens)
+    bits = W.sign_bits(d)
+    keys = _keys(rng, (B, Hkv, t_cap, d), torch.float16)
+    q = _keys(rng, (B, Hkv * G, d), torch.float16, scale=1.0)
+    packed, norms = m.quantize_keys(keys.to(DEV), bits, b)
+    out = torch.full((B, Hkv * G, T), SENTINEL, device=DEV)
+    m.score(q.to(DEV), packed, norms, bits, b, T=T, out=out,
+            lens=torch.tensor(lens, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    s = A.signs_from_bits(bits)
+    c, _ = A.lloyd_max_codebook(d, b)
+    qprime = A.transform_queries(f64(q), s)
+    got = f64(out)
+    gidx_all = A.unpack_indices(words_u32(packed[:, :, :T]), d, b)
+    onorm_all = A.key_norms(f64(keys[:, :, :T]))
+    for bi, length in enumerate(lens):
+        n_tok = min(max(length, 0), T)
+        assert np.all(got[bi, :, n_tok:] == SENTINEL), f"bi={bi} wrote past its length"
+        if n_tok:
+            assert_scores(got[bi:bi + 1, :, :n_tok], qprime[bi:bi + 1],
+                          gidx_all[bi:bi + 1, :, :n_tok], onorm_all[bi:bi + 1, :, :n_tok], c,
+                          f"ragged G={G} b={b} bi={bi}")
+
+
+def test_score_ragged_full_lengths_equal_dense_scores():
+    m = axr()
+    rng = np.random.default_rng(31)
+    d, b, B, Hkv, G, T = 128, 3, 3, 2, 4, 3000
+    bits = W.sign_bits(d)
+    keys = _keys(rng, (B, Hkv, T, d), torch.float16)
+    q = _keys(rng, (B, Hkv * G, d), torch.float16, scale=1.0).to(DEV)
+    packed, norms = m.quantize_keys(keys.to(DEV), bits, b)
+    dense = m.score(q, packed, norms, bits, b)
+    ragged = m.score(q, packed, norms, bits, b,
+                     lens=torch.full((B,), T, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(dense, ragged)
+
+
+@pytest.mark.parametrize("b", [3, 4])
+def test_decode_loop(b):
+    """Four decode steps over sequences of different lengths: each step
+    appends a key per (sequence, KV head) at the end of its sequence and
+    scores the new query against everything written so far."""
+    m = axr()
+    rng = np.random.default_rng(40 + b)
+    d, B, Hkv, G, t_cap = 128, 3, 2, 4, 700
+    lens = np.array([100, 333, 690], dtype=np.int64)
+    bits = W.sign_bits(d)
+    s = A.signs_from_bits(bits)
+    c, _ = A.lloyd_max_codebook(d, b)
+    keys = _keys(rng, (B, Hkv, t_cap, d), torch.bfloat16)
+    packed, norms = m.quantize_keys(keys.to(DEV), bits, b)
+    for step in range(4):
+        new = _keys(rng, (B, Hkv, d), torch.bfloat16)
+        q = _keys(rng, (B, Hkv * G, d), torch.bfloat16, scale=1.0)
+        pos = lens.copy()
+        m.append_keys(new.to(DEV), bits, b, packed, norms,
+                      torch.tensor(pos, dtype=torch.int32, device=DEV))
+        for bi in range(B):
+            keys[bi, :, pos[bi]] = new[bi]
+        lens += 1
+        out = torch.full((B, Hkv * G, t_cap), SENTINEL, device=DEV)
+        m.score(q.to(DEV), packed, norms, bits, b, out=out,
+                lens=torch.tensor(lens, dtype=torch.int32, device=DEV))
+        torch.cuda.synchronize()
+        _check_appended(new, packed, norms, pos.tolist(), bits, b, f"step {step}")
+        got = f64(out)
+        qprime = A.transform_queries(f64(q), s)
+        for bi in range(B):
+            n_tok = int(lens[bi])
+            assert np.all(got[bi, :, n_tok:] == SENTINEL)
+            gidx = A.unpack_indices(words_u32(packed[bi:bi + 1, :, :n_tok]), d, b)
+            onorm = A.key_norms(f64(keys[bi:bi + 1, :, :n_tok]))
+            assert_scores(got[bi:bi + 1, :, :n_tok], qprime[bi:bi + 1], gidx, onorm, c,
+                          f"step {step} bi={bi}")
+
+
+def test_decode_step_llama_full_size_sampled():
+    """The LLaMA-3.1-8B-shaped cache (8 x 8 KV heads x 32768 tokens, 32 query
+    heads, d=128, b=3) in the benchmark's decode-step configuration: append at
+    ragged positions, then score each sequence up to its new length.  Checked
+    on the appended slots and a token sample, which the oracle computes one by
+    one."""
+    m = axr()
+    w = W.llama_decode()
+    B, Hkv, T, d = w["keys"].shape
+    b, bits = w["b"], w["sign_bits"]
+    keys = w["keys"].to(DEV)
+    packed, norms = m.quantize_keys(keys, bits, b)
+    rng = np.random.default_rng(77)
+    pos = rng.integers(T // 2, T, size=B)
+    pos[0] = T - 1
+    new = _keys(rng, (B, Hkv, d), torch.float16)
+    m.append_keys(new.to(DEV), bits, b, packed, norms,
+                  torch.tensor(pos, dtype=torch.int32, device=DEV))
+    lens = torch.tensor(pos + 1, dtype=torch.int32, device=DEV)
+    out = torch.full((B, w["q"].shape[1], T), SENTINEL, device=DEV)
+    m.score(w["q"].to(DEV), packed, norms, bits, b, out=out, lens=lens)
+    torch.cuda.synchronize()
+    _check_appended(new, packed, norms, pos.tolist(), bits, b, "llama decode")
+    s = A.signs_from_bits(bits)
+    c, _ = A.lloyd_max_codebook(d, b)
+    qprime = A.transform_queries(f64(w["q"]), s)
+    kc = w["keys"].clone()
+    for bi in range(B):
+        kc[bi, :, pos[bi]] = new[bi]
+    toks = W.sample_rows(T, 96)
+    for bi in range(B):
+        n_tok = int(pos[bi]) + 1
+        sel = np.unique(np.concatenate([toks[toks < n_tok], [n_tok - 1]]))
+        tt = torch.from_numpy(sel)
+        gidx = A.unpack_indices(words_u32(packed[bi:bi + 1, :, tt]), d, b)
+        onorm = A.key_norms(f64(kc[bi:bi + 1, :, tt]))
+        assert_scores(f64(out[bi:bi + 1, :, tt]), qprime[bi:bi + 1], gidx, onorm, c,
+                      f"llama decode bi={bi}")
+        after = f64(out[bi, :, n_tok:])
+        assert np.all(after == SENTINEL)
