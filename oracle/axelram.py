@@ -65,6 +65,7 @@ __all__ = [
     "multiplications_per_query",
     "append_keys",
     "read_path_ragged",
+    "softmax_probs",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -344,6 +345,30 @@ def read_path_ragged(q, packed, norms, signs, b: int, lens, T: int):
         n_tok = min(max(int(length), 0), T)
         out[bi, :, :n_tok] = full[bi, :, :n_tok]
     return out
+
+
+def softmax_probs(scores, lens, scale: float):
+    """Attention weights from scores [B, Hq, T]: for row bi and
+    t < n = min(max(lens[bi], 0), T),
+        probs = exp(scale * s - M) / L,  M = max scale * s,  L = sum exp(scale * s - M),
+    and lse = M + log L.  Entries t >= n are NaN; an empty row has lse = -inf.
+    (The usual normalisation of attention scores; the scores are the
+    table-lookup scores of the read path.)"""
+    s = np.asarray(scores, dtype=np.float64)
+    nb, hq, T = s.shape
+    probs = np.full(s.shape, np.nan)
+    lse = np.full((nb, hq), -np.inf)
+    for bi, length in enumerate(np.asarray(lens).tolist()):
+        n_tok = min(max(int(length), 0), T)
+        if n_tok == 0:
+            continue
+        x = scale * s[bi, :, :n_tok]
+        m = x.max(axis=-1, keepdims=True)
+        e = np.exp(x - m)
+        total = e.sum(axis=-1, keepdims=True)
+        probs[bi, :, :n_tok] = e / total
+        lse[bi] = (m + np.log(total))[:, 0]
+    return probs, lse
 
 
 def dequantize_then_dot(q, idx, norms, signs, centroids) -> np.ndarray:

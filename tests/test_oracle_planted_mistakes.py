@@ -138,3 +138,35 @@ def test_ragged_length_off_by_one_is_caught(monkeypatch):
                         lambda q, p, n, s, b, lens, T: orig(q, p, n, s, b, np.asarray(lens) + 1, T))
     with pytest.raises(AssertionError):
         D.test_read_path_ragged_is_read_path_on_each_prefix()
+
+
+def test_softmax_without_max_shift_is_caught(monkeypatch):
+    # mistake: exponentiate the raw scores (no max subtraction)
+    from tests import test_oracle_softmax as S
+
+    def naive(scores, lens, scale):
+        s = np.asarray(scores, np.float64)
+        p = np.full(s.shape, np.nan)
+        lse = np.full(s.shape[:2], -np.inf)
+        for bi, n in enumerate(np.asarray(lens).tolist()):
+            n = min(max(int(n), 0), s.shape[2])
+            if n:
+                e = np.exp(scale * s[bi, :, :n])
+                p[bi, :, :n] = e / e.sum(axis=-1, keepdims=True)
+                lse[bi] = np.log(e.sum(axis=-1))
+        return p, lse
+    monkeypatch.setattr(A, "softmax_probs", naive)
+    with np.errstate(over="ignore", invalid="ignore"):
+        with pytest.raises(AssertionError):
+            S.test_large_scores_do_not_overflow()
+
+
+def test_softmax_over_the_whole_row_is_caught(monkeypatch):
+    # mistake: normalise over all T tokens instead of the row's length
+    from tests import test_oracle_softmax as S
+    orig = A.softmax_probs
+    monkeypatch.setattr(A, "softmax_probs",
+                        lambda s_, lens, scale: orig(s_, np.full(len(lens), np.shape(s_)[2]),
+                                                     scale))
+    with pytest.raises(AssertionError):
+        S.test_equals_scipy_on_each_prefix(1.0)
