@@ -172,6 +172,16 @@ def main():
     append_ms = per_launch_ms(append, args.steps)
     decode_ms = per_launch_ms(decode_step, args.steps)
 
+    # Attention probabilities: scores with split-T softmax partials, then the
+    # row normalisation (scale 1/sqrt(d)); written over `scores`.
+    log("softmax timing")
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(8, axr.score_softmax_workspace_bytes(B, Hq, Hkv, T, d, b)),
+                     dtype=torch.uint8, device=dev)
+    softmax_ms = per_launch_ms(
+        lambda: axr.score_softmax(q, packed, norms, bits, b, out=scores, lse=lse, workspace=ws),
+        args.steps)
+
     # Score kernel alone on a cold cache: read 2 GiB between launches, which
     # evicts the 136 MiB working set from the 256 MB Infinity Cache and L2
     # without leaving dirty lines behind.
@@ -253,6 +263,8 @@ def main():
                       "traffic": counter_traffic("score")},
             "score_cold_cache": {"ms_median": cold_ms, "keys_per_s": n / (cold_ms * 1e-3),
                                  "GB_per_s": cold_gbs, "frac_hbm": cold_gbs / HBM_PEAK_GBS},
+            "score_softmax": {"ms": softmax_ms, "keys_per_s": n / (softmax_ms * 1e-3),
+                              "note": "score kernel with split-T partials + row normalisation"},
             "decode_step": {"ms": decode_ms, "append_ms": append_ms,
                             "appended_keys": B * Hkv, "scored_keys": n,
                             "note": "append one key per (sequence, KV head) + ragged score"},

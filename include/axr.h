@@ -148,6 +148,37 @@ int axr_score_ragged(const void* q, int q_dtype, const uint32_t* packed, const f
                      int64_t T, int64_t t_cap, int d, int b, float* scores, void* stream);
 
 /*
+ * Attention probabilities over the table-lookup scores, with the context split
+ * across blocks.  The pages define the scores (AXELRAM, Abstract: score =
+ * norm times the sum of table entries); the softmax over a row is the usual
+ * normalisation that turns such scores into attention weights.  For batch
+ * row bi, query head h and t < len(bi) = min(max(lens[bi], 0), T) (len = T
+ * when lens is NULL):
+ *   probs[bi][h][t] = exp(scale*s_t - M) / L,  M = max_t scale*s_t,
+ *   L = sum_t exp(scale*s_t - M),  lse[bi][h] = M + log L,
+ * where s is what axr_score(_ragged) returns; probs[bi][h][t] for t >= len
+ * is not written, and an empty row gets lse = -inf.  Each tile of a row
+ * leaves (max, sum of exps) in `workspace`; a second kernel merges them and
+ * normalises the row in place.
+ *   scale     : finite multiplier of the scores (1/sqrt(d) for scaled
+ *               dot-product attention)
+ *   probs     : device float [B][Hq][T] (output), 4-byte aligned
+ *   lse       : device float [B][Hq] or NULL
+ *   workspace : device memory of at least the size axr_score_softmax_workspace
+ *               reports for the same (B, Hq, Hkv, T, d, b), 8-byte aligned;
+ *               owned by the caller, contents on entry are ignored
+ * Otherwise as axr_score_ragged.  Errors: AXR_EINVAL (also for a workspace
+ * that is too small or a non-finite scale), AXR_EUNSUPPORTED, AXR_EALIGN,
+ * AXR_EHIP.
+ */
+int axr_score_softmax_workspace(int B, int Hq, int Hkv, int64_t T, int d, int b,
+                                int64_t* bytes);
+int axr_score_softmax(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
+                      const uint32_t* sign_bits, int B, int Hq, int Hkv, const int32_t* lens,
+                      int64_t T, int64_t t_cap, int d, int b, float scale, float* probs,
+                      float* lse, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * Diagnostic export of the write-path transform (the same device code the
  * quantizer runs): y[i] = H_d (s * x[i]) / sqrt(d), divided by ||x[i]|| when
  * normalize != 0 (y = 0 for a zero row).

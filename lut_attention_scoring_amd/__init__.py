@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "AxrError", "LIB_PATH", "lib", "version", "codebook", "sign_words",
-    "packed_words", "quantize_keys", "append_keys", "score", "transform", "probe_read_stream",
+    "packed_words", "quantize_keys", "append_keys", "score", "score_softmax", "transform",
+    "probe_read_stream",
     "probe_read_write",
     "F32", "F16", "BF16",
 ]
@@ -64,6 +65,12 @@ def _load():
     so.axr_score_ragged.restype = i32
     so.axr_score_ragged.argtypes = [vp, i32, vp, vp, u32p, i32, i32, i32, i32p, i64, i64, i32,
                                     i32, vp, vp]
+    so.axr_score_softmax_workspace.restype = i32
+    so.axr_score_softmax_workspace.argtypes = [i32, i32, i32, i64, i32, i32,
+                                               ctypes.POINTER(ctypes.c_int64)]
+    so.axr_score_softmax.restype = i32
+    so.axr_score_softmax.argtypes = [vp, i32, vp, vp, u32p, i32, i32, i32, vp, i64, i64, i32,
+                                     i32, ctypes.c_float, vp, vp, vp, i64, vp]
     so.axr_transform.restype = i32
     so.axr_transform.argtypes = [vp, i32, i64, i32, u32p, i32, vp, vp]
     so.axr_probe_read_stream.restype = i32
@@ -197,6 +204,49 @@ def score(q: torch.Tensor, packed: torch.Tensor, norms: torch.Tensor, sign_bits,
                                     norms.data_ptr(), wp, B, Hq, Hkv, lens.data_ptr(), T, t_cap,
                                     d, b, out.data_ptr(), _stream(q)))
     return out
+
+
+def score_softmax_workspace_bytes(B: int, Hq: int, Hkv: int, T: int, d: int, b: int) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib.axr_score_softmax_workspace(B, Hq, Hkv, T, d, b, ctypes.byref(n)))
+    return int(n.value)
+
+
+def score_softmax(q: torch.Tensor, packed: torch.Tensor, norms: torch.Tensor, sign_bits,
+                  b: int, scale: float = None, T: int = None, lens: torch.Tensor = None,
+                  out: torch.Tensor = None, lse: torch.Tensor = None,
+                  workspace: torch.Tensor = None):
+    """Attention probabilities softmax(scale * scores) over each row's tokens
+    t < lens[bi] (all T when lens is None); returns (probs [B, Hq, T], lse
+    [B, Hq]).  scale defaults to 1/sqrt(d).  The workspace for the split-T
+    partials is allocated here unless given."""
+    B, Hq, d = q.shape
+    Bk, Hkv, t_cap, W = packed.shape
+    if Bk != B or W != packed_words(d, b) or tuple(norms.shape) != (B, Hkv, t_cap):
+        raise ValueError("q, packed and norms shapes disagree")
+    T = t_cap if T is None else int(T)
+    scale = 1.0 / float(d) ** 0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    need = score_softmax_workspace_bytes(B, Hq, Hkv, T, d, b)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=q.device)
+    _need_cuda(q, packed, norms, out, lse, workspace)
+    if tuple(out.shape) != (B, Hq, T) or tuple(lse.shape) != (B, Hq):
+        raise ValueError("out or lse has the wrong shape")
+    if lens is not None:
+        if lens.dtype != torch.int32 or tuple(lens.shape) != (B,):
+            raise ValueError("lens must be an int32 tensor of shape [B]")
+        _need_cuda(lens)
+    words, wp = _words_ptr(sign_words(sign_bits))
+    _check(lib.axr_score_softmax(q.data_ptr(), _dtype_code(q), packed.data_ptr(),
+                                 norms.data_ptr(), wp, B, Hq, Hkv,
+                                 None if lens is None else lens.data_ptr(), T, t_cap, d, b,
+                                 scale, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream(q)))
+    return out, lse
 
 
 def transform(x: torch.Tensor, sign_bits, normalize: bool = True, out: torch.Tensor = None):

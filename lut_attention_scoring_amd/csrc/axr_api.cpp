@@ -137,9 +137,9 @@ int axr_append_keys(const void* keys, int dtype, int B, int Hkv, int d, int b,
                       axr::kWriteQuantize, stream, pos, t_cap, Hkv > 0 ? Hkv : 1);
 }
 
-static int score_common(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
-                        const uint32_t* sign_bits, int B, int Hq, int Hkv, const int32_t* lens,
-                        int64_t T, int64_t t_cap, int d, int b, float* scores, void* stream) {
+// Validates the sizes shared by every read-path call.
+static int check_score_sizes(int d, int b, int q_dtype, const uint32_t* sign_bits, int B, int Hq,
+                             int Hkv, int64_t T, int64_t t_cap) {
   int rc = check_common(d, b, q_dtype, sign_bits);
   if (rc != AXR_OK) return rc;
   if (B < 0 || Hq < 0 || Hkv < 0 || T < 0)
@@ -149,19 +149,17 @@ static int score_common(const void* q, int q_dtype, const uint32_t* packed, cons
   if (Hq % Hkv != 0) return fail(AXR_EINVAL, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (t_cap < T) return fail(AXR_EINVAL, "t_cap=%lld is smaller than T=%lld",
                              static_cast<long long>(t_cap), static_cast<long long>(T));
-  const int G = Hq / Hkv;
-  if (G > 64) return fail(AXR_EUNSUPPORTED, "Hq/Hkv=%d exceeds 64", G);
+  if (Hq / Hkv > 64) return fail(AXR_EUNSUPPORTED, "Hq/Hkv=%d exceeds 64", Hq / Hkv);
   // one (batch, KV head) row of records is addressed with 32-bit offsets
   if (T > 0 && T * static_cast<int64_t>(d) * b / 8 > INT32_MAX)
     return fail(AXR_EUNSUPPORTED, "T=%lld tokens exceed 2 GiB of records per row",
                 static_cast<long long>(T));
-  if (B == 0 || T == 0) return ok();
-  if (q == nullptr || packed == nullptr || norms == nullptr || scores == nullptr)
-    return fail(AXR_EINVAL, "q, packed, norms and scores must be non-null");
-  if (!aligned(q, 16)) return fail(AXR_EALIGN, "q must be 16-byte aligned");
-  if (!aligned(packed, 16)) return fail(AXR_EALIGN, "packed must be 16-byte aligned");
-  if (!aligned(norms, 4) || !aligned(scores, 4))
-    return fail(AXR_EALIGN, "norms and scores must be 4-byte aligned");
+  return AXR_OK;
+}
+
+// Score-kernel parameters for validated sizes (everything but the tiling).
+static axr::ScoreParams score_params(const uint32_t* sign_bits, int Hq, int Hkv, int64_t T,
+                                     int64_t t_cap, int d, int b, const int32_t* lens) {
   axr::ScoreParams p;
   std::memset(&p, 0, sizeof(p));
   fill_signs(p.sign, sign_bits, d);
@@ -171,10 +169,34 @@ static int score_common(const void* q, int q_dtype, const uint32_t* packed, cons
   p.t_cap = t_cap;
   p.Hq = Hq;
   p.Hkv = Hkv;
-  p.G = G;
+  p.G = Hq / Hkv;
   p.lens = lens;
+  return p;
+}
+
+static int score_common(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
+                        const uint32_t* sign_bits, int B, int Hq, int Hkv, const int32_t* lens,
+                        int64_t T, int64_t t_cap, int d, int b, float* scores, void* stream) {
+  int rc = check_score_sizes(d, b, q_dtype, sign_bits, B, Hq, Hkv, T, t_cap);
+  if (rc != AXR_OK) return rc;
+  if (B == 0 || T == 0) return ok();
+  if (q == nullptr || packed == nullptr || norms == nullptr || scores == nullptr)
+    return fail(AXR_EINVAL, "q, packed, norms and scores must be non-null");
+  if (!aligned(q, 16)) return fail(AXR_EALIGN, "q must be 16-byte aligned");
+  if (!aligned(packed, 16)) return fail(AXR_EALIGN, "packed must be 16-byte aligned");
+  if (!aligned(norms, 4) || !aligned(scores, 4))
+    return fail(AXR_EALIGN, "norms and scores must be 4-byte aligned");
+  const axr::ScoreParams p = score_params(sign_bits, Hq, Hkv, T, t_cap, d, b, lens);
   int err = axr::launch_score(q, q_dtype, packed, norms, B, d, b, p, scores, stream);
   return hip_status(err, "score kernel launch");
+}
+
+// Tiles per score row for these sizes (sizes already validated).
+static int score_tiles(const uint32_t* sign_bits, int B, int Hq, int Hkv, int64_t T,
+                       int64_t t_cap, int d, int b, axr::ScoreParams* plan) {
+  const axr::ScoreParams p = score_params(sign_bits, Hq, Hkv, T, t_cap, d, b, nullptr);
+  return axr::launch_score(nullptr, AXR_F32, nullptr, nullptr, B, d, b, p, nullptr, nullptr,
+                           plan);
 }
 
 int axr_score(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
@@ -182,6 +204,57 @@ int axr_score(const void* q, int q_dtype, const uint32_t* packed, const float* n
               int d, int b, float* scores, void* stream) {
   return score_common(q, q_dtype, packed, norms, sign_bits, B, Hq, Hkv, nullptr, T, t_cap, d, b,
                       scores, stream);
+}
+
+int axr_score_softmax_workspace(int B, int Hq, int Hkv, int64_t T, int d, int b,
+                                int64_t* bytes) {
+  if (bytes == nullptr) return fail(AXR_EINVAL, "bytes is null");
+  static const uint32_t zero_signs[axr::kMaxSignWords] = {};
+  int rc = check_score_sizes(d, b, AXR_F32, zero_signs, B, Hq, Hkv, T, T);
+  if (rc != AXR_OK) return rc;
+  if (B == 0 || T == 0) {
+    *bytes = 0;
+    return ok();
+  }
+  axr::ScoreParams plan;
+  int err = score_tiles(zero_signs, B, Hq, Hkv, T, T, d, b, &plan);
+  if (err != 0) return fail(AXR_EUNSUPPORTED, "no launch configuration for these sizes");
+  *bytes = static_cast<int64_t>(B) * Hq * plan.tiles * 2 * static_cast<int64_t>(sizeof(float));
+  return ok();
+}
+
+int axr_score_softmax(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
+                      const uint32_t* sign_bits, int B, int Hq, int Hkv, const int32_t* lens,
+                      int64_t T, int64_t t_cap, int d, int b, float scale, float* probs,
+                      float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
+  int rc = check_score_sizes(d, b, q_dtype, sign_bits, B, Hq, Hkv, T, t_cap);
+  if (rc != AXR_OK) return rc;
+  if (!std::isfinite(scale)) return fail(AXR_EINVAL, "scale must be finite");
+  if (B == 0 || T == 0) return ok();
+  if (q == nullptr || packed == nullptr || norms == nullptr || probs == nullptr)
+    return fail(AXR_EINVAL, "q, packed, norms and probs must be non-null");
+  if (workspace == nullptr) return fail(AXR_EINVAL, "workspace is null");
+  if (!aligned(q, 16)) return fail(AXR_EALIGN, "q must be 16-byte aligned");
+  if (!aligned(packed, 16)) return fail(AXR_EALIGN, "packed must be 16-byte aligned");
+  if (!aligned(norms, 4) || !aligned(probs, 4) || (lse != nullptr && !aligned(lse, 4)) ||
+      (lens != nullptr && !aligned(lens, 4)))
+    return fail(AXR_EALIGN, "norms, probs, lse and lens must be 4-byte aligned");
+  if (!aligned(workspace, 8)) return fail(AXR_EALIGN, "workspace must be 8-byte aligned");
+  axr::ScoreParams plan;
+  if (score_tiles(sign_bits, B, Hq, Hkv, T, t_cap, d, b, &plan) != 0)
+    return fail(AXR_EUNSUPPORTED, "no launch configuration for these sizes");
+  const int64_t need = static_cast<int64_t>(B) * Hq * plan.tiles * 2 * 4;
+  if (workspace_bytes < need)
+    return fail(AXR_EINVAL, "workspace of %lld bytes is smaller than the %lld required",
+                static_cast<long long>(workspace_bytes), static_cast<long long>(need));
+  axr::ScoreParams p = score_params(sign_bits, Hq, Hkv, T, t_cap, d, b, lens);
+  p.partials = static_cast<float*>(workspace);
+  p.scale = scale;
+  int err = axr::launch_score(q, q_dtype, packed, norms, B, d, b, p, probs, stream);
+  if (err != 0) return hip_status(err, "score kernel launch");
+  err = axr::launch_softmax(probs, p.partials, lens, B, Hq, T, plan.tiles, plan.tile_len, scale,
+                            lse, stream);
+  return hip_status(err, "softmax kernel launch");
 }
 
 int axr_score_ragged(const void* q, int q_dtype, const uint32_t* packed, const float* norms,

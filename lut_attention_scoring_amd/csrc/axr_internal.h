@@ -47,13 +47,27 @@ struct ScoreParams {
   int tiles;                      // token tiles per row
   int64_t tile_len;               // tokens per tile
   const int32_t* lens;            // optional device [B]: tokens scored per batch row (<= T)
+  // Optional split-T softmax partials, [B][Hq][tiles] pairs (m, l): the
+  // largest scale * score of the tile and sum over the tile of
+  // exp(scale * score - m); (-inf, 0) for a tile with no tokens.
+  float* partials;
+  float scale;
 };
 
 // Launchers (return a hipError_t value as int; 0 = success).
 int launch_write(const void* keys, int dtype, int64_t n, int d, int b, const WriteParams& p,
                  uint32_t* packed, float* norms, float* y, int mode, void* stream);
+// With plan != nullptr nothing is launched: *plan receives the parameters
+// (tiles, tile_len, head grouping) that a launch with the same sizes uses.
 int launch_score(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
-                 int B, int d, int b, const ScoreParams& p, float* scores, void* stream);
+                 int B, int d, int b, const ScoreParams& p, float* scores, void* stream,
+                 ScoreParams* plan = nullptr);
+// Softmax over each score row from the split-T partials: in place,
+// scores[bi][h][t] = exp(scale * s - M) / L for t < len(bi), with (M, L) the
+// combined partials of the row; lse[bi][h] = M + log L when lse != nullptr.
+int launch_softmax(float* scores, const float* partials, const int32_t* lens, int B, int Hq,
+                   int64_t T, int tiles, int64_t tile_len, float scale, float* lse,
+                   void* stream);
 
 // Mode of the write kernel: quantize (indices + norms) or transform export.
 enum WriteMode { kWriteQuantize = 0, kWriteTransform = 1, kWriteTransformNormalized = 2 };

@@ -65,6 +65,24 @@ __device__ __forceinline__ uint32_t quad_reduce_scatter(const uint32_t (&a)[4]) 
   return dpp_add<1>(k0, k1);                    // head u
 }
 
+// Running (max, sum of exp(x - max)) of a stream of finite values x, one
+// exponential per value; starts from (-inf, 0).
+__device__ __forceinline__ void lse_push(float& m, float& l, float x) {
+  const float dx = x - m;                       // +inf while the stream is empty
+  const float e = __expf(-fabsf(dx));
+  l = dx > 0.0f ? fmaf(l, e, 1.0f) : l + e;
+  m = fmaxf(m, x);
+}
+
+// Merges two (max, sum) pairs; an empty pair is (-inf, 0).
+__device__ __forceinline__ void lse_merge(float& m, float& l, float m2, float l2) {
+  const float mm = fmaxf(m, m2);
+  if (mm != -INFINITY) {
+    l = l * __expf(m - mm) + l2 * __expf(m2 - mm);
+    m = mm;
+  }
+}
+
 // Butterfly stage of the query transform across lanes at distance M: the
 // lane with bit M clear keeps a + b, its partner a - b (lane holds R values).
 template <int M, int R>
@@ -180,7 +198,14 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
     len = l < 0 ? 0 : (l < prm.T ? l : prm.T);
   }
   const int64_t t0 = static_cast<int64_t>(tile) * prm.tile_len;
-  if (t0 >= len) return;                        // block-uniform: nothing to score
+  if (t0 >= len) {                              // block-uniform: nothing to score
+    if (prm.partials != nullptr && tid < nvalid) {
+      float* part = prm.partials + ((static_cast<size_t>(bi) * prm.Hq + h0 + tid) * prm.tiles + tile) * 2;
+      part[0] = -INFINITY;
+      part[1] = 0.0f;
+    }
+    return;
+  }
   const int64_t t1 = (t0 + prm.tile_len < len) ? t0 + prm.tile_len : len;
   const size_t rowbase = static_cast<size_t>(row) * prm.t_cap;
 
@@ -377,6 +402,18 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   // 3. stream the tile, keeping PD batches of records in flight and working
   //    on IL of them at once (independent lookups interleave in the LDS
   //    queue).  A batch past the tile end is computed but not stored.
+  // softmax partials of the heads this lane stores: with four lanes per key
+  // heads 4 * k + u (k < NT), otherwise head u
+  constexpr int NSLOT = S::LPK == 4 ? NT : 1;
+  const bool want_lse = prm.partials != nullptr;
+  const float lse_scale = prm.scale;
+  float sm_m[NSLOT], sm_l[NSLOT];
+#pragma unroll
+  for (int k = 0; k < NSLOT; ++k) {
+    sm_m[k] = -INFINITY;
+    sm_l[k] = 0.0f;
+  }
+
   const char* lut_bytes = reinterpret_cast<const char*>(lut);
   for (int64_t tb0 = tw; tb0 < t1; tb0 += PD * KPB) {
 #pragma unroll
@@ -431,12 +468,13 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
             const uint32_t a4[4] = {acc[il][4 * t4], acc[il][4 * t4 + 1], acc[il][4 * t4 + 2],
                                     acc[il][4 * t4 + 3]};
             const uint32_t tot = quad_reduce_scatter(a4);
+            const float sv =
+                nk[il] * (static_cast<float>(static_cast<int32_t>(tot)) * ginv_u[t4]);
             if (valid && 4 * t4 + u < nvalid) {
-              __builtin_amdgcn_raw_buffer_store_b32(
-                  __builtin_bit_cast(uint32_t, nk[il] * (static_cast<float>(
-                                                   static_cast<int32_t>(tot)) * ginv_u[t4])),
-                  rsc, vsc[t4], tb_rel * 4u, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), rsc,
+                                                    vsc[t4], tb_rel * 4u, 0);
             }
+            if (want_lse && valid) lse_push(sm_m[t4], sm_l[t4], sv * lse_scale);
           }
         } else {
           // sum over the LPK lanes of the key (exact integer sums)
@@ -453,11 +491,39 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
               if (g % S::LPK == u && g < nvalid) {
                 const float sc = static_cast<float>(static_cast<int32_t>(acc[il][g])) * ginv[g];
                 scores[(static_cast<size_t>(bi) * prm.Hq + h0 + g) * prm.T + t] = nk[il] * sc;
+                if (want_lse) lse_push(sm_m[0], sm_l[0], nk[il] * sc * lse_scale);
               }
             }
           }
         }
       }
+    }
+  }
+
+  // Split-T softmax partials of this tile: merge the lanes that hold the same
+  // head (lane bits above the key's LPK lanes), then the waves, through LDS.
+  if (want_lse) {
+    __shared__ float red[NTHREADS / 64][GB][2];
+#pragma unroll
+    for (int k = 0; k < NSLOT; ++k) {
+      float m = sm_m[k], l = sm_l[k];
+      if constexpr (S::LPK <= 4) lse_merge(m, l, lane_xor<4>(m), lane_xor<4>(l));
+      if constexpr (S::LPK <= 8) lse_merge(m, l, lane_xor<8>(m), lane_xor<8>(l));
+      lse_merge(m, l, lane_xor<16>(m), lane_xor<16>(l));
+      lse_merge(m, l, lane_xor<32>(m), lane_xor<32>(l));
+      const int head = S::LPK == 4 ? 4 * k + lane : lane;
+      if (lane < S::LPK && head < GB) {
+        red[wave][head][0] = m;
+        red[wave][head][1] = l;
+      }
+    }
+    __syncthreads();
+    if (tid < nvalid) {
+      float m = -INFINITY, l = 0.0f;
+      for (int w = 0; w < NTHREADS / 64; ++w) lse_merge(m, l, red[w][tid][0], red[w][tid][1]);
+      float* part = prm.partials + ((static_cast<size_t>(bi) * prm.Hq + h0 + tid) * prm.tiles + tile) * 2;
+      part[0] = m;
+      part[1] = l;
     }
   }
 }
@@ -476,7 +542,7 @@ constexpr bool fits() { return table_bytes<D, BITS, pick_p<D, BITS, NT>()>(NT) <
 
 template <int D, int BITS, int NT>
 int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms, int B,
-              ScoreParams p, float* scores, hipStream_t s) {
+              ScoreParams p, float* scores, hipStream_t s, ScoreParams* plan) {
   constexpr int P = pick_p<D, BITS, NT>();
   constexpr int tbytes = table_bytes<D, BITS, P>(NT);
   constexpr int bytes = tbytes + 4 * NT * D * 4 + 2 * 4 * NT * 4;  // + q' + scales
@@ -501,6 +567,10 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
   p.tile_len = tile_len;
   const int64_t grid = rows * tiles;
   if (grid > 0x7FFFFFFF) return static_cast<int>(hipErrorInvalidValue);
+  if (plan != nullptr) {                        // planning only: report the tiling
+    *plan = p;
+    return 0;
+  }
   hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS>), dim3(static_cast<unsigned>(grid)),
                      dim3(NTHREADS), 0, s, q, qdt, packed, norms, scores, p);
   return static_cast<int>(hipGetLastError());
@@ -509,32 +579,33 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
 // Eight heads per block when G >= 8 and both tables fit; otherwise four.
 template <int D, int BITS>
 int launch_b(const void* q, int qdt, const uint32_t* packed, const float* norms, int B,
-             const ScoreParams& p, float* scores, hipStream_t s) {
+             const ScoreParams& p, float* scores, hipStream_t s, ScoreParams* plan) {
   if constexpr (fits<D, BITS, 2>()) {
-    if (p.G >= 8) return launch_nt<D, BITS, 2>(q, qdt, packed, norms, B, p, scores, s);
+    if (p.G >= 8) return launch_nt<D, BITS, 2>(q, qdt, packed, norms, B, p, scores, s, plan);
   }
-  return launch_nt<D, BITS, 1>(q, qdt, packed, norms, B, p, scores, s);
+  return launch_nt<D, BITS, 1>(q, qdt, packed, norms, B, p, scores, s, plan);
 }
 
 template <int D>
 int launch_d(const void* q, int qdt, const uint32_t* packed, const float* norms, int B, int b,
-             const ScoreParams& p, float* scores, hipStream_t s) {
+             const ScoreParams& p, float* scores, hipStream_t s, ScoreParams* plan) {
   switch (b) {
-    case 2: return launch_b<D, 2>(q, qdt, packed, norms, B, p, scores, s);
-    case 3: return launch_b<D, 3>(q, qdt, packed, norms, B, p, scores, s);
-    default: return launch_b<D, 4>(q, qdt, packed, norms, B, p, scores, s);
+    case 2: return launch_b<D, 2>(q, qdt, packed, norms, B, p, scores, s, plan);
+    case 3: return launch_b<D, 3>(q, qdt, packed, norms, B, p, scores, s, plan);
+    default: return launch_b<D, 4>(q, qdt, packed, norms, B, p, scores, s, plan);
   }
 }
 
 }  // namespace
 
 int launch_score(const void* q, int q_dtype, const uint32_t* packed, const float* norms, int B,
-                 int d, int b, const ScoreParams& p, float* scores, void* stream) {
+                 int d, int b, const ScoreParams& p, float* scores, void* stream,
+                 ScoreParams* plan) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (d) {
-    case 128: return launch_d<128>(q, q_dtype, packed, norms, B, b, p, scores, s);
-    case 256: return launch_d<256>(q, q_dtype, packed, norms, B, b, p, scores, s);
-    default: return launch_d<512>(q, q_dtype, packed, norms, B, b, p, scores, s);
+    case 128: return launch_d<128>(q, q_dtype, packed, norms, B, b, p, scores, s, plan);
+    case 256: return launch_d<256>(q, q_dtype, packed, norms, B, b, p, scores, s, plan);
+    default: return launch_d<512>(q, q_dtype, packed, norms, B, b, p, scores, s, plan);
   }
 }
 

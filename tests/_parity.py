@@ -58,3 +58,33 @@ def assert_norms(gpu_norms, ora_norms, label=""):
     g = np.asarray(gpu_norms, np.float64)
     o = np.asarray(ora_norms, np.float64)
     assert np.all(np.abs(g - o) <= NORM_RTOL * o), f"{label}: norm mismatch"
+
+
+def softmax_bounds(ref_scores, cond, scale, n_tok):
+    """Per-element bound on |log p_gpu - log p_ref| for one row's first n_tok
+    tokens (p_ref from the exact scores of the GPU's indices).  The score
+    error bound eps_t = SCORE_RTOL * cond_t moves log p_t by at most
+    scale * (eps_t + max eps) (the log-sum-exp moves by at most scale * max
+    eps); fp32 adds rounding of the exponent argument and of the exponentials,
+    the split sums and the division: 2^-22 (|scale s_t - M| + 2 |M|) + 8e-6."""
+    x = scale * np.asarray(ref_scores, np.float64)[..., :n_tok]
+    eps = SCORE_RTOL * np.asarray(cond, np.float64)[..., :n_tok]
+    m = x.max(axis=-1, keepdims=True)
+    bound = scale * (eps + eps.max(axis=-1, keepdims=True)) + 2.0 ** -22 * (
+        np.abs(x - m) + 2 * np.abs(m)) + 8e-6
+    lse_bound = (scale * eps.max(axis=-1) + 2.0 ** -22 * np.abs(m[..., 0]) * 2 + 8e-6)
+    return bound, lse_bound
+
+
+def assert_softmax(gpu_probs, gpu_lse, ref_scores, cond, scale, n_tok, label=""):
+    """gpu_probs [Hq, T] and gpu_lse [Hq] of one batch row against the oracle
+    softmax of ref_scores [Hq, T] (exact scores of the GPU's indices)."""
+    p_ref, lse_ref = A.softmax_probs(np.asarray(ref_scores)[None], [n_tok], scale)
+    p_ref, lse_ref = p_ref[0, :, :n_tok], lse_ref[0]
+    bound, lse_bound = softmax_bounds(ref_scores, cond, scale, n_tok)
+    got = np.asarray(gpu_probs, np.float64)[:, :n_tok]
+    err = np.abs(got - p_ref)
+    ok = err <= p_ref * np.expm1(bound) + 2.0 ** -126
+    assert np.all(ok), f"{label}: probability error {float((err / np.maximum(p_ref, 1e-300)).max()):.3e}"
+    lerr = np.abs(np.asarray(gpu_lse, np.float64) - lse_ref)
+    assert np.all(lerr <= lse_bound), f"{label}: lse error {float(lerr.max()):.3e}"
