@@ -66,6 +66,9 @@ __all__ = [
     "append_keys",
     "read_path_ragged",
     "softmax_probs",
+    "dense_scores",
+    "sign_selection_errors",
+    "select_sign_pattern",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -369,6 +372,52 @@ def softmax_probs(scores, lens, scale: float):
         probs[bi, :, :n_tok] = e / total
         lse[bi] = (m + np.log(total))[:, 0]
     return probs, lse
+
+
+def dense_scores(q, keys) -> np.ndarray:
+    """Exact scores q_h . k_t in float64 for q [B, Hq, d], keys [B, Hkv, T, d]
+    (query head h reads KV head h // (Hq / Hkv))."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(keys, dtype=np.float64)
+    nb, hq, _ = q.shape
+    g = hq // k.shape[1]
+    out = np.empty((nb, hq, k.shape[2]))
+    for bi in range(nb):
+        for h in range(hq):
+            out[bi, h] = k[bi, h // g] @ q[bi, h]
+    return out
+
+
+def sign_selection_errors(keys, q, candidate_bits, b: int) -> np.ndarray:
+    """Objective terms of the one-time sign-pattern selection (AXELRAM,
+    Abstract: gradient-free, a few hundred candidates, a few calibration
+    samples).  The page's objective is perplexity, which needs model weights;
+    the stand-in measures how far the table scores are from the exact scores:
+    for candidate c and calibration sample i,
+        err[c, i] = sum (s_lut - s_exact)^2,   ref[c, i] = sum s_exact^2
+    over every (batch, query head, token) of the sample.  keys
+    [S, B, Hkv, T, d], q [S, B, Hq, d], candidate_bits [C, d].
+    Returns [C, S, 2] (err, ref)."""
+    keys = np.asarray(keys, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    out = np.empty((len(candidate_bits), keys.shape[0], 2))
+    exact = [dense_scores(q[i], keys[i]) for i in range(keys.shape[0])]
+    for c, bits in enumerate(candidate_bits):
+        s = signs_from_bits(bits)
+        for i in range(keys.shape[0]):
+            w = write_path(keys[i], s, b)
+            lut = read_path(q[i], w["packed"], w["norms"], s, b)
+            out[c, i, 0] = np.sum((lut - exact[i]) ** 2)
+            out[c, i, 1] = np.sum(exact[i] ** 2)
+    return out
+
+
+def select_sign_pattern(errors):
+    """The candidate whose worst calibration sample has the smallest relative
+    score error sqrt(err / ref); returns (index, objective per candidate)."""
+    e = np.asarray(errors, dtype=np.float64)
+    objective = np.sqrt(e[..., 0] / e[..., 1]).max(axis=1)
+    return int(np.argmin(objective)), objective
 
 
 def dequantize_then_dot(q, idx, norms, signs, centroids) -> np.ndarray:

@@ -170,3 +170,34 @@ def test_softmax_over_the_whole_row_is_caught(monkeypatch):
                                                      scale))
     with pytest.raises(AssertionError):
         S.test_equals_scipy_on_each_prefix(1.0)
+
+
+def test_absolute_selection_error_is_caught(monkeypatch):
+    # mistake: rank candidates by absolute error, so the loudest layer decides
+    from tests import test_oracle_signsel as P
+    orig = A.sign_selection_errors
+
+    def absolute(keys, q, cands, b):
+        e = orig(keys, q, cands, b)
+        e[..., 1] = 1.0
+        return e
+    monkeypatch.setattr(A, "sign_selection_errors", absolute)
+    with pytest.raises(AssertionError):
+        P.test_sample_scale_does_not_change_relative_error()
+
+
+def test_selection_gqa_mapping_mistake_is_caught(monkeypatch):
+    # mistake: query head h reads KV head h % Hkv
+    from tests import test_oracle_signsel as P
+
+    def wrong(q, keys):
+        q = np.asarray(q, np.float64)
+        k = np.asarray(keys, np.float64)
+        out = np.empty((q.shape[0], q.shape[1], k.shape[2]))
+        for bi in range(q.shape[0]):
+            for h in range(q.shape[1]):
+                out[bi, h] = k[bi, h % k.shape[1]] @ q[bi, h]
+        return out
+    monkeypatch.setattr(A, "dense_scores", wrong)
+    with pytest.raises(AssertionError):
+        P.test_dense_scores_gqa_mapping()

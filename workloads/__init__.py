@@ -103,6 +103,49 @@ def write_sweep(d: int = 128, b: int = 3, B: int = 1, Hkv: int = 8, T: int = 327
     return {"keys": keys, "q": None, "sign_bits": sign_bits(d), "b": b}
 
 
+SIGN_CANDIDATES = 200
+CALIBRATION_SAMPLES = 8
+
+
+def sign_candidates(d: int, count: int = SIGN_CANDIDATES, seed: int = 105) -> np.ndarray:
+    """Candidate sign patterns for the one-time selection, as bits [count, d]:
+    candidate 0 is the default pattern (seed 1), candidate i > 0 draws d bits
+    from PCG64 seeded with (seed, i)."""
+    out = np.empty((count, d), dtype=np.uint8)
+    out[0] = sign_bits(d)
+    for i in range(1, count):
+        out[i] = np.random.default_rng([seed, i]).integers(0, 2, size=d)
+    return out
+
+
+def calibration_samples(count: int = CALIBRATION_SAMPLES, B: int = 1, Hkv: int = 2,
+                        Hq: int = 16, T: int = 2048, d: int = 128, seed: int = 106):
+    """Calibration set for the sign-pattern selection: `count` synthetic layers
+    shaped like the Qwen2.5-3B layers (per-layer norm scale exp(U[ln 1,
+    ln 100]), per-token jitter U[0.8, 1.2]) with log-normal channel scales
+    exp(g), g ~ N(0,1) per (KV head, channel), and a mean vector mu ~ N(0,1)
+    per (KV head, channel) shared over tokens (keys of real layers are not
+    centred; without a shared direction every sign pattern is equivalent):
+        keys = (z * exp(g) + mu) * S_l * j,  z ~ N(0, 1);  q ~ N(0, 1).
+    Returns keys [count, B, Hkv, T, d] and q [count, B, Hq, d], fp16."""
+    children = np.random.SeedSequence(seed).spawn(count)
+    keys = np.empty((count, B, Hkv, T, d), dtype=np.float32)
+    q = np.empty((count, B, Hq, d), dtype=np.float32)
+    scales = []
+    for i, child in enumerate(children):
+        rng = np.random.default_rng(child)
+        s_l = float(np.exp(rng.uniform(0.0, np.log(100.0))))
+        g = rng.standard_normal((Hkv, d))
+        mu = rng.standard_normal((Hkv, d))
+        jitter = rng.uniform(0.8, 1.2, size=(B, Hkv, T, 1))
+        z = rng.standard_normal((B, Hkv, T, d))
+        keys[i] = (z * np.exp(g)[None, :, None, :] + mu[None, :, None, :]) * jitter * s_l
+        q[i] = rng.standard_normal((B, Hq, d))
+        scales.append(s_l)
+    return {"keys": _to(keys, torch.float16), "q": _to(q, torch.float16),
+            "layer_scale": np.array(scales)}
+
+
 # The five workloads at full size, by name.
 FULL_SIZES = {
     "tiny_d128_b3_n4096": dict(B=1, Hkv=1, Hq=1, T=4096, d=128, b=3, dtype="f32"),
