@@ -213,6 +213,19 @@ def main():
                               args.steps)
     del flush, sink
 
+    # One-time sign-pattern selection: 200 candidates on 8 calibration layers
+    # (B=1, 2 KV heads, 16 query heads, 2048 tokens, b=4).
+    log("sign-pattern selection timing")
+    cal = W.calibration_samples()
+    cal_k, cal_q = cal["keys"].to(dev), cal["q"].to(dev)
+    cands = W.sign_candidates(d)
+    axr.sign_selection_errors(cal_k, cal_q, cands[:2], 4)
+    torch.cuda.synchronize()
+    t_sel = time.perf_counter()
+    sel_idx, sel_obj = axr.select_sign_pattern(cal_k, cal_q, cands, 4)
+    sel_ms = (time.perf_counter() - t_sel) * 1e3
+    del cal_k, cal_q
+
     write_bytes_per_key = d * keys.element_size() + d * b // 8 + 4
     score_bytes_per_key = d * b // 8 + 4 + 4 * (Hq // Hkv)
     write_bytes = n * write_bytes_per_key
@@ -265,6 +278,13 @@ def main():
                                  "GB_per_s": cold_gbs, "frac_hbm": cold_gbs / HBM_PEAK_GBS},
             "score_softmax": {"ms": softmax_ms, "keys_per_s": n / (softmax_ms * 1e-3),
                               "note": "score kernel with split-T partials + row normalisation"},
+            "sign_selection": {"ms": sel_ms, "candidates": len(cands),
+                               "calibration_samples": int(cal["keys"].shape[0]),
+                               "keys_per_sample": int(cal["keys"][0].numel() // d),
+                               "chosen": sel_idx,
+                               "objective_default": float(sel_obj[0]),
+                               "objective_chosen": float(sel_obj[sel_idx]),
+                               "objective_worst": float(sel_obj.max())},
             "decode_step": {"ms": decode_ms, "append_ms": append_ms,
                             "appended_keys": B * Hkv, "scored_keys": n,
                             "note": "append one key per (sequence, KV head) + ragged score"},

@@ -179,6 +179,34 @@ int axr_score_softmax(const void* q, int q_dtype, const uint32_t* packed, const 
                       float* lse, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * One-time sign-pattern selection (AXELRAM, Abstract: gradient-free, a few
+ * hundred candidate sign patterns, a few calibration samples, chosen once).
+ * The pages rank candidates by perplexity, which needs model weights; this
+ * call measures instead how far the table scores are from the exact scores.
+ * For candidate c (sign words candidates[c*d/32 .. c*d/32 + d/32), HOST) and
+ * calibration sample i, the calibration keys are quantized with that pattern
+ * and scored against the sample's queries, and
+ *   errors[(c*S + i)*2 + 0] = sum (s_lut - s_exact)^2
+ *   errors[(c*S + i)*2 + 1] = sum s_exact^2
+ * over every (batch, query head, token) of the sample, accumulated in fp64
+ * (s_exact = q . k in fp32).  The caller picks, e.g., the candidate whose
+ * worst sample has the smallest sqrt(err / ref).
+ *   keys      : device [S][B][Hkv][T][d] of `dtype`, 16-byte aligned
+ *   q         : device [S][B][Hq][d] of `q_dtype`, 16-byte aligned
+ *   errors    : device double [C][S][2], 8-byte aligned
+ *   workspace : device memory of the size axr_sign_selection_workspace
+ *               reports, 256-byte aligned, owned by the caller
+ * C, S, B or T = 0 is a no-op.  Same size limits as axr_score.  Errors:
+ * AXR_EINVAL, AXR_EUNSUPPORTED, AXR_EALIGN, AXR_EHIP.
+ */
+int axr_sign_selection_workspace(int S, int B, int Hq, int Hkv, int64_t T, int d, int b,
+                                 int64_t* bytes);
+int axr_sign_selection_errors(const void* keys, int dtype, const void* q, int q_dtype, int S,
+                              int B, int Hq, int Hkv, int64_t T, int d, int b,
+                              const uint32_t* candidates, int C, double* errors,
+                              void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * Diagnostic export of the write-path transform (the same device code the
  * quantizer runs): y[i] = H_d (s * x[i]) / sqrt(d), divided by ||x[i]|| when
  * normalize != 0 (y = 0 for a zero row).

@@ -20,6 +20,7 @@ import torch
 __all__ = [
     "AxrError", "LIB_PATH", "lib", "version", "codebook", "sign_words",
     "packed_words", "quantize_keys", "append_keys", "score", "score_softmax", "transform",
+    "sign_selection_errors", "select_sign_pattern",
     "probe_read_stream",
     "probe_read_write",
     "F32", "F16", "BF16",
@@ -71,6 +72,12 @@ def _load():
     so.axr_score_softmax.restype = i32
     so.axr_score_softmax.argtypes = [vp, i32, vp, vp, u32p, i32, i32, i32, vp, i64, i64, i32,
                                      i32, ctypes.c_float, vp, vp, vp, i64, vp]
+    so.axr_sign_selection_workspace.restype = i32
+    so.axr_sign_selection_workspace.argtypes = [i32, i32, i32, i32, i64, i32, i32,
+                                                ctypes.POINTER(ctypes.c_int64)]
+    so.axr_sign_selection_errors.restype = i32
+    so.axr_sign_selection_errors.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i64, i32, i32,
+                                             u32p, i32, vp, vp, i64, vp]
     so.axr_transform.restype = i32
     so.axr_transform.argtypes = [vp, i32, i64, i32, u32p, i32, vp, vp]
     so.axr_probe_read_stream.restype = i32
@@ -247,6 +254,41 @@ def score_softmax(q: torch.Tensor, packed: torch.Tensor, norms: torch.Tensor, si
                                  scale, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(), _stream(q)))
     return out, lse
+
+
+def sign_selection_errors(keys: torch.Tensor, q: torch.Tensor, candidate_bits, b: int):
+    """Per-candidate, per-sample score errors of the sign-pattern selection:
+    keys [S, B, Hkv, T, d], q [S, B, Hq, d], candidate_bits [C, d] (host)
+    -> float64 device tensor [C, S, 2] of (sum (s_lut - s_exact)^2,
+    sum s_exact^2)."""
+    S, B, Hkv, T, d = keys.shape
+    Sq, Bq, Hq, dq = q.shape
+    if (Sq, Bq, dq) != (S, B, d):
+        raise ValueError("keys and q shapes disagree")
+    bits = np.asarray(candidate_bits).reshape(-1, d)
+    C = bits.shape[0]
+    words = np.ascontiguousarray(np.stack([sign_words(r) for r in bits]) if C else
+                                 np.zeros((0, d // 32)), dtype=np.uint32)
+    wp = words.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))
+    nbytes = ctypes.c_int64(0)
+    _check(lib.axr_sign_selection_workspace(S, B, Hq, Hkv, T, d, b, ctypes.byref(nbytes)))
+    ws = torch.empty(max(256, nbytes.value), dtype=torch.uint8, device=keys.device)
+    errors = torch.zeros(C, S, 2, dtype=torch.float64, device=keys.device)
+    _need_cuda(keys, q, errors, ws)
+    _check(lib.axr_sign_selection_errors(keys.data_ptr(), _dtype_code(keys), q.data_ptr(),
+                                         _dtype_code(q), S, B, Hq, Hkv, T, d, b, wp, C,
+                                         errors.data_ptr(), ws.data_ptr(), ws.numel(),
+                                         _stream(keys)))
+    return errors
+
+
+def select_sign_pattern(keys: torch.Tensor, q: torch.Tensor, candidate_bits, b: int):
+    """The candidate whose worst calibration sample has the smallest relative
+    score error sqrt(err / ref); returns (index, objective per candidate as a
+    numpy array).  Synchronises with the device to read the errors."""
+    e = sign_selection_errors(keys, q, candidate_bits, b).cpu().numpy()
+    objective = np.sqrt(e[..., 0] / e[..., 1]).max(axis=1)
+    return int(np.argmin(objective)), objective
 
 
 def transform(x: torch.Tensor, sign_bits, normalize: bool = True, out: torch.Tensor = None):

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libaxr.so")
 
 SOURCES = ["axr_api.cpp", "axr_codebook.cpp", "axr_write.hip", "axr_score.hip",
-           "axr_softmax.hip", "axr_probe.hip"]
+           "axr_softmax.hip", "axr_select.hip", "axr_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -76,6 +76,22 @@ int axr_codebook(int d, int b, double* centroids, double* thresholds) {
   return ok();
 }
 
+// Write-kernel parameters: sign words and the positive thresholds scaled by
+// sqrt(d) (the kernel compares against them times the key's norm).
+static axr::WriteParams write_params(const uint32_t* sign_bits, int d, int b) {
+  axr::WriteParams p;
+  std::memset(&p, 0, sizeof(p));
+  fill_signs(p.sign, sign_bits, d);
+  const axr::Codebook& cb = axr::cached_codebook(d, b);
+  const int half = 1 << (b - 1);
+  const double sqrt_d = std::sqrt(static_cast<double>(d));
+  for (int i = 0; i + 1 < half; ++i) p.tpos[i] = static_cast<float>(cb.threshold[half + i] * sqrt_d);
+  p.inv_sqrt_d = static_cast<float>(1.0 / sqrt_d);
+  p.t_cap = 0;
+  p.Hkv = 1;
+  return p;
+}
+
 static int write_common(const void* x, int dtype, int64_t n, int d, int b,
                         const uint32_t* sign_bits, uint32_t* packed, float* norms, float* y,
                         int mode, void* stream, const int32_t* pos = nullptr,
@@ -95,14 +111,7 @@ static int write_common(const void* x, int dtype, int64_t n, int d, int b,
     if (y == nullptr) return fail(AXR_EINVAL, "y is null");
     if (!aligned(y, 16)) return fail(AXR_EALIGN, "y must be 16-byte aligned");
   }
-  axr::WriteParams p;
-  std::memset(&p, 0, sizeof(p));
-  fill_signs(p.sign, sign_bits, d);
-  const axr::Codebook& cb = axr::cached_codebook(d, b);
-  const int half = 1 << (b - 1);
-  const double sqrt_d = std::sqrt(static_cast<double>(d));
-  for (int i = 0; i + 1 < half; ++i) p.tpos[i] = static_cast<float>(cb.threshold[half + i] * sqrt_d);
-  p.inv_sqrt_d = static_cast<float>(1.0 / sqrt_d);
+  axr::WriteParams p = write_params(sign_bits, d, b);
   p.pos = pos;
   p.t_cap = t_cap;
   p.Hkv = Hkv;
@@ -255,6 +264,91 @@ int axr_score_softmax(const void* q, int q_dtype, const uint32_t* packed, const 
   err = axr::launch_softmax(probs, p.partials, lens, B, Hq, T, plan.tiles, plan.tile_len, scale,
                             lse, stream);
   return hip_status(err, "softmax kernel launch");
+}
+
+// Workspace layout of the sign-pattern selection (offsets 256-byte aligned):
+// exact scores, table scores (fp32 [S*B][Hq][T] each), records and norms of
+// the calibration keys.
+struct SelectLayout {
+  int64_t exact, lut, packed, norms, total;
+};
+
+static SelectLayout select_layout(int S, int B, int Hq, int Hkv, int64_t T, int d, int b) {
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  const int64_t rows = static_cast<int64_t>(S) * B;
+  const int64_t n_scores = rows * Hq * T, n_keys = rows * Hkv * T;
+  SelectLayout l;
+  l.exact = 0;
+  l.lut = up(l.exact + n_scores * 4);
+  l.packed = up(l.lut + n_scores * 4);
+  l.norms = up(l.packed + n_keys * (static_cast<int64_t>(d) * b / 8));
+  l.total = up(l.norms + n_keys * 4);
+  return l;
+}
+
+static int check_select_sizes(int S, int B, int Hq, int Hkv, int64_t T, int d, int b,
+                              int dtype, int q_dtype) {
+  static const uint32_t zero_signs[axr::kMaxSignWords] = {};
+  if (S < 0) return fail(AXR_EINVAL, "S=%d is negative", S);
+  int rc = check_score_sizes(d, b, q_dtype, zero_signs, B, Hq, Hkv, T, T);
+  if (rc != AXR_OK) return rc;
+  if (!supported_dtype(dtype)) return fail(AXR_EUNSUPPORTED, "dtype=%d is not supported", dtype);
+  if (static_cast<int64_t>(S) * B > INT32_MAX / 2)
+    return fail(AXR_EUNSUPPORTED, "S*B=%lld is too large", static_cast<long long>(S) * B);
+  return AXR_OK;
+}
+
+int axr_sign_selection_workspace(int S, int B, int Hq, int Hkv, int64_t T, int d, int b,
+                                 int64_t* bytes) {
+  if (bytes == nullptr) return fail(AXR_EINVAL, "bytes is null");
+  int rc = check_select_sizes(S, B, Hq, Hkv, T, d, b, AXR_F32, AXR_F32);
+  if (rc != AXR_OK) return rc;
+  *bytes = select_layout(S, B, Hq, Hkv, T, d, b).total;
+  return ok();
+}
+
+int axr_sign_selection_errors(const void* keys, int dtype, const void* q, int q_dtype, int S,
+                              int B, int Hq, int Hkv, int64_t T, int d, int b,
+                              const uint32_t* candidates, int C, double* errors,
+                              void* workspace, int64_t workspace_bytes, void* stream) {
+  int rc = check_select_sizes(S, B, Hq, Hkv, T, d, b, dtype, q_dtype);
+  if (rc != AXR_OK) return rc;
+  if (C < 0) return fail(AXR_EINVAL, "C=%d is negative", C);
+  if (C == 0 || S == 0 || B == 0 || T == 0) return ok();
+  if (candidates == nullptr) return fail(AXR_EINVAL, "candidates is null");
+  if (keys == nullptr || q == nullptr || errors == nullptr || workspace == nullptr)
+    return fail(AXR_EINVAL, "keys, q, errors and workspace must be non-null");
+  if (!aligned(keys, 16) || !aligned(q, 16)) return fail(AXR_EALIGN, "keys and q must be 16-byte aligned");
+  if (!aligned(errors, 8)) return fail(AXR_EALIGN, "errors must be 8-byte aligned");
+  if (!aligned(workspace, 256)) return fail(AXR_EALIGN, "workspace must be 256-byte aligned");
+  const SelectLayout lay = select_layout(S, B, Hq, Hkv, T, d, b);
+  if (workspace_bytes < lay.total)
+    return fail(AXR_EINVAL, "workspace of %lld bytes is smaller than the %lld required",
+                static_cast<long long>(workspace_bytes), static_cast<long long>(lay.total));
+  char* ws = static_cast<char*>(workspace);
+  float* exact = reinterpret_cast<float*>(ws + lay.exact);
+  float* lut = reinterpret_cast<float*>(ws + lay.lut);
+  uint32_t* packed = reinterpret_cast<uint32_t*>(ws + lay.packed);
+  float* norms = reinterpret_cast<float*>(ws + lay.norms);
+  const int rows = S * B;
+  const int64_t n = static_cast<int64_t>(rows) * Hkv * T;
+  int err = axr::launch_dense_scores(keys, dtype, q, q_dtype, rows, Hq, Hkv, T, d, exact, stream);
+  if (err != 0) return hip_status(err, "exact-score kernel launch");
+  const int words = d / 32;
+  for (int c = 0; c < C; ++c) {
+    const uint32_t* sc = candidates + static_cast<size_t>(c) * words;
+    const axr::WriteParams wp = write_params(sc, d, b);
+    err = axr::launch_write(keys, dtype, n, d, b, wp, packed, norms, nullptr, axr::kWriteQuantize,
+                            stream);
+    if (err != 0) return hip_status(err, "write kernel launch");
+    const axr::ScoreParams sp = score_params(sc, Hq, Hkv, T, T, d, b, nullptr);
+    err = axr::launch_score(q, q_dtype, packed, norms, rows, d, b, sp, lut, stream);
+    if (err != 0) return hip_status(err, "score kernel launch");
+    err = axr::launch_score_error(lut, exact, S, static_cast<int64_t>(B) * Hq * T,
+                                  errors + static_cast<size_t>(c) * S * 2, stream);
+    if (err != 0) return hip_status(err, "error kernel launch");
+  }
+  return ok();
 }
 
 int axr_score_ragged(const void* q, int q_dtype, const uint32_t* packed, const float* norms,

@@ -69,6 +69,14 @@ int launch_softmax(float* scores, const float* partials, const int32_t* lens, in
                    int64_t T, int tiles, int64_t tile_len, float scale, float* lse,
                    void* stream);
 
+// Sign-pattern selection: exact fp32 scores for rows x Hq x T from keys
+// [rows][Hkv][T][d] and q [rows][Hq][d]; per-sample fp64 error sums
+// (err[2i] = sum (lut - exact)^2, err[2i+1] = sum exact^2 over `per` scores).
+int launch_dense_scores(const void* keys, int kdt, const void* q, int qdt, int rows, int Hq,
+                        int Hkv, int64_t T, int d, float* out, void* stream);
+int launch_score_error(const float* lut, const float* exact, int samples, int64_t per,
+                       double* err, void* stream);
+
 // Mode of the write kernel: quantize (indices + norms) or transform export.
 enum WriteMode { kWriteQuantize = 0, kWriteTransform = 1, kWriteTransformNormalized = 2 };
 

@@ -191,3 +191,46 @@ def test_score_ragged_validation():
     assert _r(q=None)[0] == axr.EINVAL
     assert _r(lens=None, B=0, q=None, packed=None, norms=None, scores=None)[0] == axr.OK
     assert _r(lens=None, T=0, t_cap=0, q=None, packed=None, norms=None, scores=None)[0] == axr.OK
+
+
+def test_softmax_validation():
+    n = ctypes.c_int64(-1)
+    f = axr.lib.axr_score_softmax_workspace
+    assert _status(f, 2, 8, 2, 64, 128, 3, ctypes.byref(n))[0] == axr.OK and n.value > 0
+    assert _status(f, 2, 8, 2, 64, 128, 3, None)[0] == axr.EINVAL
+    assert _status(f, 2, 6, 4, 64, 128, 3, ctypes.byref(n))[0] == axr.EINVAL
+    assert _status(f, 0, 8, 2, 64, 128, 3, ctypes.byref(n))[0] == axr.OK and n.value == 0
+    g = axr.lib.axr_score_softmax
+
+    def sm(ws=FAKE, ws_bytes=1 << 20, scale=0.1, probs=FAKE, lse=None, lens=None):
+        return _status(g, FAKE, axr.F16, FAKE, FAKE, SIGNS, 2, 8, 2, lens, 64, 64, 128, 3,
+                       ctypes.c_float(scale), probs, lse, ws, ws_bytes, None)
+    assert sm(ws=None)[0] == axr.EINVAL
+    assert sm(ws_bytes=8)[0] == axr.EINVAL
+    assert sm(scale=float("inf"))[0] == axr.EINVAL
+    assert sm(probs=None)[0] == axr.EINVAL
+    assert sm(ws=FAKE + 4)[0] == axr.EALIGN
+    assert sm(lse=FAKE + 2)[0] == axr.EALIGN
+
+
+def test_sign_selection_validation():
+    n = ctypes.c_int64(-1)
+    f = axr.lib.axr_sign_selection_workspace
+    assert _status(f, 8, 1, 16, 2, 2048, 128, 4, ctypes.byref(n))[0] == axr.OK
+    assert n.value >= 8 * 16 * 2048 * 8
+    assert _status(f, -1, 1, 16, 2, 2048, 128, 4, ctypes.byref(n))[0] == axr.EINVAL
+    assert _status(f, 8, 1, 16, 2, 2048, 100, 4, ctypes.byref(n))[0] == axr.EUNSUPPORTED
+    g = axr.lib.axr_sign_selection_errors
+    cands = (ctypes.c_uint32 * 8)()
+
+    def sel(keys=FAKE, dtype=axr.F16, C=2, cand=cands, errors=FAKE, ws=FAKE, ws_bytes=1 << 40):
+        return _status(g, keys, dtype, FAKE, axr.F16, 3, 1, 16, 2, 128, 128, 3, cand, C, errors,
+                       ws, ws_bytes, None)
+    assert sel(cand=None)[0] == axr.EINVAL
+    assert sel(C=-1)[0] == axr.EINVAL
+    assert sel(keys=None)[0] == axr.EINVAL
+    assert sel(dtype=9)[0] == axr.EUNSUPPORTED
+    assert sel(ws_bytes=16)[0] == axr.EINVAL
+    assert sel(ws=FAKE + 16)[0] == axr.EALIGN
+    assert sel(errors=FAKE + 4)[0] == axr.EALIGN
+    assert sel(C=0, keys=None, cand=None, errors=None, ws=None)[0] == axr.OK
