@@ -69,6 +69,13 @@ __all__ = [
     "dense_scores",
     "sign_selection_errors",
     "select_sign_pattern",
+    "quaternion_multiply",
+    "quaternion_conjugate",
+    "isoquant_rotate",
+    "isoquant_unrotate",
+    "isoquant_write_path",
+    "reconstruction_mse",
+    "rotation_fmas",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -418,6 +425,92 @@ def select_sign_pattern(errors):
     e = np.asarray(errors, dtype=np.float64)
     objective = np.sqrt(e[..., 0] / e[..., 1]).max(axis=1)
     return int(np.argmin(objective)), objective
+
+
+# ---------------------------------------------------------------------------
+# Comparison transform: block-wise quaternion rotations ("IsoQuant:
+# Hardware-Aligned SO(4) Isoclinic Rotations for LLM KV Cache Compression",
+# arXiv 2603.28430, Abstract).  Each block of 4 coordinates
+# (v[4m], v[4m+1], v[4m+2], v[4m+3]) is the quaternion w + x i + y j + z k;
+# IsoQuant-Full maps it to q_L v conj(q_R), IsoQuant-Fast to q_L v, with
+# unit quaternions q_L, q_R per block.  Used with the same Lloyd-Max
+# quantizer as the Walsh-Hadamard path.
+# ---------------------------------------------------------------------------
+
+def quaternion_multiply(a, b) -> np.ndarray:
+    """Hamilton product of quaternions stored as (w, x, y, z) on the last
+    axis, from i^2 = j^2 = k^2 = ijk = -1."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    aw, ax, ay, az = a[..., 0], a[..., 1], a[..., 2], a[..., 3]
+    bw, bx, by, bz = b[..., 0], b[..., 1], b[..., 2], b[..., 3]
+    return np.stack([aw * bw - ax * bx - ay * by - az * bz,
+                     aw * bx + ax * bw + ay * bz - az * by,
+                     aw * by - ax * bz + ay * bw + az * bx,
+                     aw * bz + ax * by - ay * bx + az * bw], axis=-1)
+
+
+def quaternion_conjugate(q) -> np.ndarray:
+    q = np.asarray(q, dtype=np.float64)
+    return q * np.array([1.0, -1.0, -1.0, -1.0])
+
+
+def isoquant_rotate(x, q_left, q_right=None) -> np.ndarray:
+    """Block rotation of x [..., d]: block m -> q_left[m] v conj(q_right[m])
+    (IsoQuant-Full), or q_left[m] v when q_right is None (IsoQuant-Fast).
+    q_left, q_right: [d/4, 4]."""
+    x = np.asarray(x, dtype=np.float64)
+    v = x.reshape(*x.shape[:-1], x.shape[-1] // 4, 4)
+    t = quaternion_multiply(np.asarray(q_left, np.float64), v)
+    if q_right is not None:
+        t = quaternion_multiply(t, quaternion_conjugate(q_right))
+    return t.reshape(x.shape)
+
+
+def isoquant_unrotate(y, q_left, q_right=None) -> np.ndarray:
+    """Inverse of isoquant_rotate for unit quaternions:
+    conj(q_left) w q_right."""
+    y = np.asarray(y, dtype=np.float64)
+    w = y.reshape(*y.shape[:-1], y.shape[-1] // 4, 4)
+    if q_right is not None:
+        w = quaternion_multiply(w, np.asarray(q_right, np.float64))
+    t = quaternion_multiply(quaternion_conjugate(q_left), w)
+    return t.reshape(y.shape)
+
+
+def isoquant_write_path(keys, q_left, q_right, b: int):
+    """The write path with the block rotation in place of the Hadamard
+    transform: unit-normalise, rotate, quantize with the Lloyd-Max codebook
+    for N(0, 1/d), pack.  q_right None selects IsoQuant-Fast."""
+    k = np.asarray(keys, dtype=np.float64)
+    d = k.shape[-1]
+    _, thresholds = lloyd_max_codebook(d, b)
+    norms = key_norms(k)
+    safe = np.where(norms > 0.0, norms, 1.0)
+    y = isoquant_rotate(k / safe[..., None], q_left, q_right)
+    y = np.where(norms[..., None] > 0.0, y, 0.0)
+    idx = quantize(y, thresholds)
+    return {"y": y, "norms": norms, "idx": idx, "packed": pack_indices(idx, b)}
+
+
+def reconstruction_mse(keys, idx, centroids, unrotate) -> float:
+    """Mean over keys of ||k/||k|| - T^-1(c[idx])||^2 (stage-1
+    quantize-dequantize error on unit vectors); `unrotate` maps rotated
+    coordinates back."""
+    k = np.asarray(keys, dtype=np.float64)
+    unit = k / key_norms(k)[..., None]
+    rec = unrotate(np.asarray(centroids, np.float64)[np.asarray(idx)])
+    return float(np.mean(np.sum((unit - rec) ** 2, axis=-1)))
+
+
+def rotation_fmas(d: int, kind: str) -> int:
+    """Multiply-adds of one forward rotation of a d-vector: a Hamilton product
+    is 16; IsoQuant-Full uses two per block of 4, IsoQuant-Fast one, and the
+    Walsh-Hadamard transform uses additions only."""
+    if kind == "wht":
+        return 0
+    per_block = {"isoquant_full": 32, "isoquant_fast": 16}[kind]
+    return per_block * (d // 4)
 
 
 def dequantize_then_dot(q, idx, norms, signs, centroids) -> np.ndarray:

@@ -201,3 +201,37 @@ def test_selection_gqa_mapping_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(A, "dense_scores", wrong)
     with pytest.raises(AssertionError):
         P.test_dense_scores_gqa_mapping()
+
+
+def test_hamilton_sign_error_is_caught(monkeypatch):
+    # mistake: one cross term of the product with the wrong sign
+    from tests import test_oracle_isoquant as Q
+
+    def wrong(a, b):
+        a = np.asarray(a, np.float64)
+        b = np.asarray(b, np.float64)
+        aw, ax, ay, az = a[..., 0], a[..., 1], a[..., 2], a[..., 3]
+        bw, bx, by, bz = b[..., 0], b[..., 1], b[..., 2], b[..., 3]
+        return np.stack([aw * bw - ax * bx - ay * by - az * bz,
+                         aw * bx + ax * bw - ay * bz - az * by,
+                         aw * by - ax * bz + ay * bw + az * bx,
+                         aw * bz + ax * by - ay * bx + az * bw], axis=-1)
+    monkeypatch.setattr(A, "quaternion_multiply", wrong)
+    with pytest.raises(AssertionError):
+        Q.test_hamilton_units()
+
+
+def test_fast_rotation_on_the_wrong_side_is_caught(monkeypatch):
+    # mistake: the Fast variant multiplies on the right (v q_L)
+    from tests import test_oracle_isoquant as Q
+    orig = A.isoquant_rotate
+
+    def wrong(x, ql, qr=None):
+        if qr is not None:
+            return orig(x, ql, qr)
+        x = np.asarray(x, np.float64)
+        v = x.reshape(*x.shape[:-1], x.shape[-1] // 4, 4)
+        return A.quaternion_multiply(v, np.asarray(ql, np.float64)).reshape(x.shape)
+    monkeypatch.setattr(A, "isoquant_rotate", wrong)
+    with pytest.raises(AssertionError):
+        Q.test_rotation_preserves_norms_and_inverts(False)

@@ -146,6 +146,14 @@ def calibration_samples(count: int = CALIBRATION_SAMPLES, B: int = 1, Hkv: int =
             "layer_scale": np.array(scales)}
 
 
+def isoquant_quaternions(d: int, seed: int = 107) -> np.ndarray:
+    """Per-block quaternion pairs for the block-rotation comparison transform:
+    [d/4, 2, 4] float32, (q_left, q_right) of block m, each a Gaussian 4-vector
+    divided by its length (a uniformly random unit quaternion)."""
+    g = np.random.default_rng(seed).standard_normal((d // 4, 2, 4))
+    return (g / np.linalg.norm(g, axis=-1, keepdims=True)).astype(np.float32)
+
+
 # The five workloads at full size, by name.
 FULL_SIZES = {
     "tiny_d128_b3_n4096": dict(B=1, Hkv=1, Hq=1, T=4096, d=128, b=3, dtype="f32"),
