@@ -213,6 +213,26 @@ def main():
                               args.steps)
     del flush, sink
 
+    # Write path with the comparison transforms (block-quaternion rotations)
+    # on the prefill write-sweep keys, b = 3.
+    log("write-transform comparison")
+    wt = {}
+    for dd in (128, 256, 512):
+        ws_keys = W.write_sweep(d=dd, b=3)["keys"].to(dev)
+        nk = ws_keys.numel() // dd
+        pk = torch.empty(nk, dd * 3 // 32, dtype=torch.int32, device=dev)
+        nm = torch.empty(nk, dtype=torch.float32, device=dev)
+        qs = torch.from_numpy(W.isoquant_quaternions(dd)).to(dev)
+        sb = W.sign_bits(dd)
+        kb = nk * (dd * 2 + dd * 3 // 8 + 4)
+        for name, fn in (
+                ("wht", lambda: axr.quantize_keys(ws_keys, sb, 3, packed=pk, norms=nm)),
+                ("isoquant_full", lambda: axr.quantize_keys_isoquant(ws_keys, qs, 3, True, pk, nm)),
+                ("isoquant_fast", lambda: axr.quantize_keys_isoquant(ws_keys, qs, 3, False, pk, nm))):
+            t_ms = per_launch_ms(fn, args.steps)
+            wt[f"d{dd}_{name}"] = {"ms": t_ms, "GB_per_s": kb / (t_ms * 1e-3) / 1e9}
+        del ws_keys, pk, nm
+
     # One-time sign-pattern selection: 200 candidates on 8 calibration layers
     # (B=1, 2 KV heads, 16 query heads, 2048 tokens, b=4).
     log("sign-pattern selection timing")
@@ -278,6 +298,7 @@ def main():
                                  "GB_per_s": cold_gbs, "frac_hbm": cold_gbs / HBM_PEAK_GBS},
             "score_softmax": {"ms": softmax_ms, "keys_per_s": n / (softmax_ms * 1e-3),
                               "note": "score kernel with split-T partials + row normalisation"},
+            "write_transforms_b3": wt,
             "sign_selection": {"ms": sel_ms, "candidates": len(cands),
                                "calibration_samples": int(cal["keys"].shape[0]),
                                "keys_per_sample": int(cal["keys"][0].numel() // d),

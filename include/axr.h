@@ -207,6 +207,26 @@ int axr_sign_selection_errors(const void* keys, int dtype, const void* q, int q_
                               void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * Comparison write path with block-quaternion rotations in place of the sign
+ * pattern + Walsh-Hadamard transform ("IsoQuant: Hardware-Aligned SO(4)
+ * Isoclinic Rotations for LLM KV Cache Compression", arXiv 2603.28430,
+ * Abstract): coordinates 4m..4m+3 of the unit key form the quaternion
+ * v = (w, x, y, z) and become q_L[m] v conj(q_R[m]) (full = 1) or q_L[m] v
+ * (full = 0); the result is quantized with the same Lloyd-Max codebook and
+ * packed in the same layout, norms as in axr_quantize_keys.
+ *   quats : device float [d/4][2][4], (q_L, q_R) of each block as (w, x, y, z),
+ *           unit length, 16-byte aligned (q_R unused when full = 0)
+ * Otherwise as axr_quantize_keys / axr_transform (y = T(x), divided by ||x||
+ * when normalize != 0).  These scores need queries rotated the same way
+ * (axr_score applies the Walsh-Hadamard transform and does not apply here).
+ */
+int axr_quantize_keys_isoquant(const void* keys, int dtype, int64_t n, int d, int b,
+                               const float* quats, int full, uint32_t* packed, float* norms,
+                               void* stream);
+int axr_transform_isoquant(const void* x, int dtype, int64_t n, int d, const float* quats,
+                           int full, int normalize, float* y, void* stream);
+
+/*
  * Diagnostic export of the write-path transform (the same device code the
  * quantizer runs): y[i] = H_d (s * x[i]) / sqrt(d), divided by ||x[i]|| when
  * normalize != 0 (y = 0 for a zero row).

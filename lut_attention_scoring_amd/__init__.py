@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "AxrError", "LIB_PATH", "lib", "version", "codebook", "sign_words",
     "packed_words", "quantize_keys", "append_keys", "score", "score_softmax", "transform",
-    "sign_selection_errors", "select_sign_pattern",
+    "sign_selection_errors", "select_sign_pattern", "quantize_keys_isoquant",
+    "transform_isoquant",
     "probe_read_stream",
     "probe_read_write",
     "F32", "F16", "BF16",
@@ -78,6 +79,10 @@ def _load():
     so.axr_sign_selection_errors.restype = i32
     so.axr_sign_selection_errors.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i64, i32, i32,
                                              u32p, i32, vp, vp, i64, vp]
+    so.axr_quantize_keys_isoquant.restype = i32
+    so.axr_quantize_keys_isoquant.argtypes = [vp, i32, i64, i32, i32, vp, i32, vp, vp, vp]
+    so.axr_transform_isoquant.restype = i32
+    so.axr_transform_isoquant.argtypes = [vp, i32, i64, i32, vp, i32, i32, vp, vp]
     so.axr_transform.restype = i32
     so.axr_transform.argtypes = [vp, i32, i64, i32, u32p, i32, vp, vp]
     so.axr_probe_read_stream.restype = i32
@@ -289,6 +294,51 @@ def select_sign_pattern(keys: torch.Tensor, q: torch.Tensor, candidate_bits, b: 
     e = sign_selection_errors(keys, q, candidate_bits, b).cpu().numpy()
     objective = np.sqrt(e[..., 0] / e[..., 1]).max(axis=1)
     return int(np.argmin(objective)), objective
+
+
+def _quats(quats: torch.Tensor, d: int, device) -> torch.Tensor:
+    if tuple(quats.shape) != (d // 4, 2, 4) or quats.dtype != torch.float32:
+        raise ValueError("quats must be float32 [d/4, 2, 4]")
+    if quats.device != device:
+        raise ValueError("quats must live on the keys' device")
+    return quats.contiguous()
+
+
+def quantize_keys_isoquant(keys: torch.Tensor, quats: torch.Tensor, b: int, full: bool = True,
+                           packed: torch.Tensor = None, norms: torch.Tensor = None):
+    """Comparison write path with block-quaternion rotations (IsoQuant-Full or
+    -Fast) instead of the Walsh-Hadamard transform; same codebook and layout."""
+    d = keys.shape[-1]
+    lead = keys.shape[:-1]
+    quats = _quats(quats, d, keys.device)
+    if packed is None:
+        packed = torch.empty(*lead, packed_words(d, b), dtype=torch.int32, device=keys.device)
+    if norms is None:
+        norms = torch.empty(*lead, dtype=torch.float32, device=keys.device)
+    _need_cuda(keys, packed, norms, quats)
+    n = keys.numel() // d if d else 0
+    if packed.numel() != n * packed_words(d, b) or norms.numel() != n:
+        raise ValueError("packed/norms sizes do not match keys")
+    _check(lib.axr_quantize_keys_isoquant(keys.data_ptr(), _dtype_code(keys), n, d, b,
+                                          quats.data_ptr(), int(bool(full)), packed.data_ptr(),
+                                          norms.data_ptr(), _stream(keys)))
+    return packed, norms
+
+
+def transform_isoquant(x: torch.Tensor, quats: torch.Tensor, full: bool = True,
+                       normalize: bool = True, out: torch.Tensor = None):
+    """Diagnostic: the block-quaternion rotation of each row (/ ||x|| if
+    normalize), fp32 [..., d]."""
+    d = x.shape[-1]
+    quats = _quats(quats, d, x.device)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _need_cuda(x, out, quats)
+    n = x.numel() // d if d else 0
+    _check(lib.axr_transform_isoquant(x.data_ptr(), _dtype_code(x), n, d, quats.data_ptr(),
+                                      int(bool(full)), int(bool(normalize)), out.data_ptr(),
+                                      _stream(x)))
+    return out
 
 
 def transform(x: torch.Tensor, sign_bits, normalize: bool = True, out: torch.Tensor = None):

@@ -78,13 +78,16 @@ int axr_codebook(int d, int b, double* centroids, double* thresholds) {
 
 // Write-kernel parameters: sign words and the positive thresholds scaled by
 // sqrt(d) (the kernel compares against them times the key's norm).
-static axr::WriteParams write_params(const uint32_t* sign_bits, int d, int b) {
+// (The block-quaternion transform is orthonormal as it stands, so there the
+// factor is 1.)
+static axr::WriteParams write_params(const uint32_t* sign_bits, int d, int b,
+                                     int tf = axr::kWht) {
   axr::WriteParams p;
   std::memset(&p, 0, sizeof(p));
-  fill_signs(p.sign, sign_bits, d);
+  if (sign_bits != nullptr) fill_signs(p.sign, sign_bits, d);
   const axr::Codebook& cb = axr::cached_codebook(d, b);
   const int half = 1 << (b - 1);
-  const double sqrt_d = std::sqrt(static_cast<double>(d));
+  const double sqrt_d = tf == axr::kWht ? std::sqrt(static_cast<double>(d)) : 1.0;
   for (int i = 0; i + 1 < half; ++i) p.tpos[i] = static_cast<float>(cb.threshold[half + i] * sqrt_d);
   p.inv_sqrt_d = static_cast<float>(1.0 / sqrt_d);
   p.t_cap = 0;
@@ -95,9 +98,15 @@ static axr::WriteParams write_params(const uint32_t* sign_bits, int d, int b) {
 static int write_common(const void* x, int dtype, int64_t n, int d, int b,
                         const uint32_t* sign_bits, uint32_t* packed, float* norms, float* y,
                         int mode, void* stream, const int32_t* pos = nullptr,
-                        int64_t t_cap = 0, int Hkv = 1) {
-  int rc = check_common(d, b, dtype, sign_bits);
+                        int64_t t_cap = 0, int Hkv = 1, int tf = axr::kWht,
+                        const float* quats = nullptr) {
+  static const uint32_t no_signs[axr::kMaxSignWords] = {};
+  int rc = check_common(d, b, dtype, tf == axr::kWht ? sign_bits : no_signs);
   if (rc != AXR_OK) return rc;
+  if (tf != axr::kWht && n > 0) {
+    if (quats == nullptr) return fail(AXR_EINVAL, "quats is null");
+    if (!aligned(quats, 16)) return fail(AXR_EALIGN, "quats must be 16-byte aligned");
+  }
   if (n < 0) return fail(AXR_EINVAL, "n=%lld is negative", static_cast<long long>(n));
   if (n == 0) return ok();
   if (x == nullptr) return fail(AXR_EINVAL, "input pointer is null");
@@ -111,11 +120,12 @@ static int write_common(const void* x, int dtype, int64_t n, int d, int b,
     if (y == nullptr) return fail(AXR_EINVAL, "y is null");
     if (!aligned(y, 16)) return fail(AXR_EALIGN, "y must be 16-byte aligned");
   }
-  axr::WriteParams p = write_params(sign_bits, d, b);
+  axr::WriteParams p = write_params(tf == axr::kWht ? sign_bits : nullptr, d, b, tf);
   p.pos = pos;
   p.t_cap = t_cap;
   p.Hkv = Hkv;
-  int err = axr::launch_write(x, dtype, n, d, b, p, packed, norms, y, mode, stream);
+  p.quats = quats;
+  int err = axr::launch_write(x, dtype, n, d, b, p, packed, norms, y, mode, stream, tf);
   return hip_status(err, "write kernel launch");
 }
 
@@ -130,6 +140,21 @@ int axr_transform(const void* x, int dtype, int64_t n, int d, const uint32_t* si
   // b only selects a kernel instance here; the transform does not depend on it.
   return write_common(x, dtype, n, d, 3, sign_bits, nullptr, nullptr, y,
                       normalize ? axr::kWriteTransformNormalized : axr::kWriteTransform, stream);
+}
+
+int axr_quantize_keys_isoquant(const void* keys, int dtype, int64_t n, int d, int b,
+                               const float* quats, int full, uint32_t* packed, float* norms,
+                               void* stream) {
+  return write_common(keys, dtype, n, d, b, nullptr, packed, norms, nullptr,
+                      axr::kWriteQuantize, stream, nullptr, 0, 1,
+                      full ? axr::kIsoFull : axr::kIsoFast, quats);
+}
+
+int axr_transform_isoquant(const void* x, int dtype, int64_t n, int d, const float* quats,
+                           int full, int normalize, float* y, void* stream) {
+  return write_common(x, dtype, n, d, 3, nullptr, nullptr, nullptr, y,
+                      normalize ? axr::kWriteTransformNormalized : axr::kWriteTransform, stream,
+                      nullptr, 0, 1, full ? axr::kIsoFull : axr::kIsoFast, quats);
 }
 
 int axr_append_keys(const void* keys, int dtype, int B, int Hkv, int d, int b,

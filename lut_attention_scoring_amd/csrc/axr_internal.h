@@ -34,7 +34,14 @@ struct WriteParams {
   const int32_t* pos;
   int64_t t_cap;
   int Hkv;
+  // Comparison transform (kIsoFull / kIsoFast): device float [d/4][2][4],
+  // (left, right) unit quaternion of each block of 4 coordinates.
+  const float* quats;
 };
+
+// Write-path transforms: the method's sign pattern + Walsh-Hadamard, and the
+// block-quaternion rotations kept for comparison (full SO(4) or one factor).
+enum WriteTransform { kWht = 0, kIsoFull = 1, kIsoFast = 2 };
 
 struct ScoreParams {
   uint32_t sign[kMaxSignWords];
@@ -56,7 +63,8 @@ struct ScoreParams {
 
 // Launchers (return a hipError_t value as int; 0 = success).
 int launch_write(const void* keys, int dtype, int64_t n, int d, int b, const WriteParams& p,
-                 uint32_t* packed, float* norms, float* y, int mode, void* stream);
+                 uint32_t* packed, float* norms, float* y, int mode, void* stream,
+                 int tf = kWht);
 // With plan != nullptr nothing is launched: *plan receives the parameters
 // (tiles, tile_len, head grouping) that a launch with the same sizes uses.
 int launch_score(const void* q, int q_dtype, const uint32_t* packed, const float* norms,

@@ -146,12 +146,38 @@ __device__ __forceinline__ uint32_t append_bit(uint32_t w, uint64_t m) {
   return r;
 }
 
+// Block rotation of the comparison transform (IsoQuant, Abstract): the four
+// coordinates v of a block, as the quaternion (w, x, y, z), become a v or,
+// with a right factor, a v conj(c) (Hamilton products, 16 multiply-adds
+// each).
+template <bool kRight>
+__device__ __forceinline__ void quat_block(float* v, const float (&a)[4], const float (&c)[4]) {
+  const float vw = v[0], vx = v[1], vy = v[2], vz = v[3];
+  const float tw = a[0] * vw - a[1] * vx - a[2] * vy - a[3] * vz;
+  const float tx = a[0] * vx + a[1] * vw + a[2] * vz - a[3] * vy;
+  const float ty = a[0] * vy - a[1] * vz + a[2] * vw + a[3] * vx;
+  const float tz = a[0] * vz + a[1] * vy - a[2] * vx + a[3] * vw;
+  if constexpr (kRight) {
+    v[0] = tw * c[0] + tx * c[1] + ty * c[2] + tz * c[3];
+    v[1] = -tw * c[1] + tx * c[0] - ty * c[3] + tz * c[2];
+    v[2] = -tw * c[2] + tx * c[3] + ty * c[0] - tz * c[1];
+    v[3] = -tw * c[3] - tx * c[2] + ty * c[1] + tz * c[0];
+  } else {
+    v[0] = tw;
+    v[1] = tx;
+    v[2] = ty;
+    v[3] = tz;
+  }
+}
+
 template <int DT>
 struct Raw {
   static constexpr int kWords = DT == AXR_F32 ? 32 : 16;  // 32-bit words per lane chunk
 };
 
-template <int D, int BITS, int DT>
+// TF selects the transform: kWht (sign pattern + Walsh-Hadamard), or the
+// block-quaternion comparison transforms kIsoFull / kIsoFast.
+template <int D, int BITS, int DT, int TF>
 __global__ __launch_bounds__(kBlock) void write_kernel(const void* __restrict__ keys, int64_t n,
                                                      WriteParams prm,
                                                      uint32_t* __restrict__ packed,
@@ -183,6 +209,19 @@ __global__ __launch_bounds__(kBlock) void write_kernel(const void* __restrict__ 
   float P[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) P[i] = prm.tpos[i];
+  // quaternions of this lane's eight blocks (comparison transform only)
+  float qa[8][4], qb[8][4];
+  if constexpr (TF != kWht) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int m = 8 * u + k;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        qa[k][c] = prm.quats[(m * 2) * 4 + c];
+        qb[k][c] = TF == kIsoFull ? prm.quats[(m * 2 + 1) * 4 + c] : 0.0f;
+      }
+    }
+  }
 
   for (int64_t base = static_cast<int64_t>(blockIdx.x) * KPB; base < n;
        base += static_cast<int64_t>(gridDim.x) * KPB) {
@@ -209,7 +248,33 @@ __global__ __launch_bounds__(kBlock) void write_kernel(const void* __restrict__ 
     // the conversion to fp32
     float ss = 0.0f;
     float x[32];
-    if constexpr (DT == AXR_F16) {
+    if constexpr (TF != kWht) {
+      // comparison transform: plain conversion, then the block rotations
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float lo, hi;
+        if constexpr (DT == AXR_F16) {
+          const half2_v h2 = __builtin_bit_cast(half2_v, raw[i]);
+          ss = __builtin_amdgcn_fdot2(h2, h2, ss, false);
+          lo = static_cast<float>(h2.x);
+          hi = static_cast<float>(h2.y);
+        } else if constexpr (DT == AXR_BF16) {
+          lo = __uint_as_float(raw[i] << 16);
+          hi = __uint_as_float(raw[i] & 0xFFFF0000u);
+          ss = fmaf(lo, lo, ss);
+          ss = fmaf(hi, hi, ss);
+        } else {
+          lo = __uint_as_float(raw[2 * i]);
+          hi = __uint_as_float(raw[2 * i + 1]);
+          ss = fmaf(lo, lo, ss);
+          ss = fmaf(hi, hi, ss);
+        }
+        x[2 * i] = lo;
+        x[2 * i + 1] = hi;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) quat_block<TF == kIsoFull>(&x[4 * k], qa[k], qb[k]);
+    } else if constexpr (DT == AXR_F16) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const uint32_t r = raw[i];
@@ -250,14 +315,16 @@ __global__ __launch_bounds__(kBlock) void write_kernel(const void* __restrict__ 
     if constexpr (LPK >= 16) ss += lane_xor<8>(ss);
     const float nrm = sqrtf(ss);
 
-    reg_stage<2>(x);
-    reg_stage<4>(x);
-    reg_stage<8>(x);
-    reg_stage<16>(x);
-    if constexpr (LPK >= 2) lane_stage<1>(x, m1);
-    if constexpr (LPK >= 4) lane_stage<2>(x, m2);
-    if constexpr (LPK >= 8) lane_stage<4>(x, m4);
-    if constexpr (LPK >= 16) lane_stage<8>(x, m8);
+    if constexpr (TF == kWht) {
+      reg_stage<2>(x);
+      reg_stage<4>(x);
+      reg_stage<8>(x);
+      reg_stage<16>(x);
+      if constexpr (LPK >= 2) lane_stage<1>(x, m1);
+      if constexpr (LPK >= 4) lane_stage<2>(x, m2);
+      if constexpr (LPK >= 8) lane_stage<4>(x, m4);
+      if constexpr (LPK >= 16) lane_stage<8>(x, m8);
+    }
 
     if (mode == kWriteQuantize) {
       float S[8];
@@ -314,46 +381,56 @@ __global__ __launch_bounds__(kBlock) void write_kernel(const void* __restrict__ 
   }
 }
 
-template <int D, int BITS, int DT>
+template <int D, int BITS, int DT, int TF>
 int launch_t(const void* keys, int64_t n, const WriteParams& p, uint32_t* packed, float* norms,
              float* y, int mode, hipStream_t s) {
   constexpr int KPB = kBlock / (D / 32);
   const int64_t need = (n + KPB - 1) / KPB;
   const int grid = static_cast<int>(need < 4096 ? need : 4096);
-  hipLaunchKernelGGL((write_kernel<D, BITS, DT>), dim3(grid), dim3(kBlock), 0, s, keys, n, p,
-                     packed, norms, y, mode);
+  hipLaunchKernelGGL((write_kernel<D, BITS, DT, TF>), dim3(grid), dim3(kBlock), 0, s, keys, n,
+                     p, packed, norms, y, mode);
   return static_cast<int>(hipGetLastError());
+}
+
+template <int D, int BITS, int DT>
+int launch_tf(const void* keys, int64_t n, const WriteParams& p, uint32_t* packed,
+              float* norms, float* y, int mode, int tf, hipStream_t s) {
+  switch (tf) {
+    case kIsoFull: return launch_t<D, BITS, DT, kIsoFull>(keys, n, p, packed, norms, y, mode, s);
+    case kIsoFast: return launch_t<D, BITS, DT, kIsoFast>(keys, n, p, packed, norms, y, mode, s);
+    default: return launch_t<D, BITS, DT, kWht>(keys, n, p, packed, norms, y, mode, s);
+  }
 }
 
 template <int D, int BITS>
 int launch_dt(const void* keys, int dtype, int64_t n, const WriteParams& p, uint32_t* packed,
-              float* norms, float* y, int mode, hipStream_t s) {
+              float* norms, float* y, int mode, int tf, hipStream_t s) {
   switch (dtype) {
-    case AXR_F32: return launch_t<D, BITS, AXR_F32>(keys, n, p, packed, norms, y, mode, s);
-    case AXR_F16: return launch_t<D, BITS, AXR_F16>(keys, n, p, packed, norms, y, mode, s);
-    default: return launch_t<D, BITS, AXR_BF16>(keys, n, p, packed, norms, y, mode, s);
+    case AXR_F32: return launch_tf<D, BITS, AXR_F32>(keys, n, p, packed, norms, y, mode, tf, s);
+    case AXR_F16: return launch_tf<D, BITS, AXR_F16>(keys, n, p, packed, norms, y, mode, tf, s);
+    default: return launch_tf<D, BITS, AXR_BF16>(keys, n, p, packed, norms, y, mode, tf, s);
   }
 }
 
 template <int D>
 int launch_b(const void* keys, int dtype, int64_t n, int b, const WriteParams& p,
-             uint32_t* packed, float* norms, float* y, int mode, hipStream_t s) {
+             uint32_t* packed, float* norms, float* y, int mode, int tf, hipStream_t s) {
   switch (b) {
-    case 2: return launch_dt<D, 2>(keys, dtype, n, p, packed, norms, y, mode, s);
-    case 3: return launch_dt<D, 3>(keys, dtype, n, p, packed, norms, y, mode, s);
-    default: return launch_dt<D, 4>(keys, dtype, n, p, packed, norms, y, mode, s);
+    case 2: return launch_dt<D, 2>(keys, dtype, n, p, packed, norms, y, mode, tf, s);
+    case 3: return launch_dt<D, 3>(keys, dtype, n, p, packed, norms, y, mode, tf, s);
+    default: return launch_dt<D, 4>(keys, dtype, n, p, packed, norms, y, mode, tf, s);
   }
 }
 
 }  // namespace
 
 int launch_write(const void* keys, int dtype, int64_t n, int d, int b, const WriteParams& p,
-                 uint32_t* packed, float* norms, float* y, int mode, void* stream) {
+                 uint32_t* packed, float* norms, float* y, int mode, void* stream, int tf) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (d) {
-    case 128: return launch_b<128>(keys, dtype, n, b, p, packed, norms, y, mode, s);
-    case 256: return launch_b<256>(keys, dtype, n, b, p, packed, norms, y, mode, s);
-    default: return launch_b<512>(keys, dtype, n, b, p, packed, norms, y, mode, s);
+    case 128: return launch_b<128>(keys, dtype, n, b, p, packed, norms, y, mode, tf, s);
+    case 256: return launch_b<256>(keys, dtype, n, b, p, packed, norms, y, mode, tf, s);
+    default: return launch_b<512>(keys, dtype, n, b, p, packed, norms, y, mode, tf, s);
   }
 }
 
