@@ -33,11 +33,11 @@ CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
 # files below); otherwise traffic is reported as null.
 COUNTER_TRAFFIC = {
     "write": {"sources": ["axr_write.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "0b21968884ccb26af253ee7bbf4f0f70f6d63d73",
-              "bytes": (262385.8 * 2.0 + 107270.5) * 1024},
+              "sha1": "ec5941c7bd91cae2728afba258fae5e71881a915",
+              "bytes": (262222.0 * 2.0 + 107143.9) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "bdcd5a0c1c87004442c9c3e7a550d30e6271713c",
-              "bytes": (53551.9 * 2.0 + 32793.2) * 1024},
+              "sha1": "6213716b7b03762e7d18bda09fe12cb808d3174c",
+              "bytes": (53565.2 * 2.0 + 32792.1) * 1024},
 }
 
 
