@@ -13,6 +13,7 @@ cache (2 GiB of reads between launches) for its HBM roofline.
 """
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -128,23 +129,34 @@ def main():
 
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gc.enable()
     ms_per_step = elapsed * 1e3 / args.steps
 
     def per_launch_ms(fn, reps):
         """Average duration of `reps` back-to-back launches of fn, from HIP
-        events recorded on the stream the kernels run on."""
+        events recorded on the stream the kernels run on.  Python's cyclic
+        garbage collector is held off inside the timed loop (a full
+        collection of this process stalls the launching thread for tens of
+        milliseconds)."""
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fn()
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
+        gc.collect()
+        gc.disable()
+        try:
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        finally:
+            gc.enable()
         return e0.elapsed_time(e1) / reps
 
     log("per-kernel timing")
@@ -171,6 +183,21 @@ def main():
 
     append_ms = per_launch_ms(append, args.steps)
     decode_ms = per_launch_ms(decode_step, args.steps)
+
+    # The same step captured once in a HIP graph and replayed (one launch
+    # per step from the host).
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        decode_step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode_step()
+    torch.cuda.synchronize()
+    decode_graph_ms = per_launch_ms(graph.replay, args.steps)
+    del graph
 
     # Attention probabilities: scores with split-T softmax partials, then the
     # row normalisation (scale 1/sqrt(d)); written over `scores`.
@@ -241,9 +268,12 @@ def main():
     cands = W.sign_candidates(d)
     axr.sign_selection_errors(cal_k, cal_q, cands[:2], 4)
     torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
     t_sel = time.perf_counter()
     sel_idx, sel_obj = axr.select_sign_pattern(cal_k, cal_q, cands, 4)
     sel_ms = (time.perf_counter() - t_sel) * 1e3
+    gc.enable()
     del cal_k, cal_q
 
     write_bytes_per_key = d * keys.element_size() + d * b // 8 + 4
@@ -306,7 +336,8 @@ def main():
                                "objective_default": float(sel_obj[0]),
                                "objective_chosen": float(sel_obj[sel_idx]),
                                "objective_worst": float(sel_obj.max())},
-            "decode_step": {"ms": decode_ms, "append_ms": append_ms,
+            "decode_step": {"ms": decode_ms, "graph_replay_ms": decode_graph_ms,
+                            "append_ms": append_ms,
                             "appended_keys": B * Hkv, "scored_keys": n,
                             "note": "append one key per (sequence, KV head) + ragged score"},
         },
