@@ -67,14 +67,14 @@ def parse():
 
 
 def cpu_baseline(w):
-    """The fp64 oracle, as it stands, on batch elements [0, 4) of the same
-    workload (4 x 8 KV heads x 32768 tokens = 1048576 keys, 32 query heads)."""
+    """The fp64 oracle, as it stands, on batch elements [0, 6) of the same
+    workload (6 x 8 KV heads x 32768 tokens = 1572864 keys, 32 query heads)."""
     import numpy as np
     import threadpoolctl
     from oracle import axelram as A
 
     import torch
-    nb = 4
+    nb = 6
     keys = w["keys"][0:nb].to(dtype=torch.float64).numpy()
     q = w["q"][0:nb].to(dtype=torch.float64).numpy()
     s = A.signs_from_bits(w["sign_bits"])
@@ -86,7 +86,7 @@ def cpu_baseline(w):
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
                    if p.get("user_api") == "blas"] or [1])
     return {"value": n / dt, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"batch elements 0-3 of 8: {n} keys (4 x 8 KV heads x 32768 tokens) "
+            "sample": f"batch elements 0-{nb - 1} of 8: {n} keys ({nb} x 8 KV heads x 32768 tokens) "
                       f"quantized and scored by 32 query heads each, fp64 numpy, {dt:.1f} s; "
                       f"host reports {os.cpu_count()} CPUs"}
 

@@ -196,7 +196,7 @@ int axr_score_softmax(const void* q, int q_dtype, const uint32_t* packed, const 
  *   errors    : device double [C][S][2], 8-byte aligned
  *   workspace : device memory of the size axr_sign_selection_workspace
  *               reports, 256-byte aligned, owned by the caller
- * C, S, B or T = 0 is a no-op.  Same size limits as axr_score.  Errors:
+ * C, S, B or T = 0 is a no-op; S <= 64.  Same size limits as axr_score.  Errors:
  * AXR_EINVAL, AXR_EUNSUPPORTED, AXR_EALIGN, AXR_EHIP.
  */
 int axr_sign_selection_workspace(int S, int B, int Hq, int Hkv, int64_t T, int d, int b,

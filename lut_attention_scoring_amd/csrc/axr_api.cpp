@@ -295,7 +295,7 @@ int axr_score_softmax(const void* q, int q_dtype, const uint32_t* packed, const 
 // exact scores, table scores (fp32 [S*B][Hq][T] each), records and norms of
 // the calibration keys.
 struct SelectLayout {
-  int64_t exact, lut, packed, norms, total;
+  int64_t exact, lut, packed, norms, partials, total;
 };
 
 static SelectLayout select_layout(int S, int B, int Hq, int Hkv, int64_t T, int d, int b) {
@@ -307,7 +307,8 @@ static SelectLayout select_layout(int S, int B, int Hq, int Hkv, int64_t T, int 
   l.lut = up(l.exact + n_scores * 4);
   l.packed = up(l.lut + n_scores * 4);
   l.norms = up(l.packed + n_keys * (static_cast<int64_t>(d) * b / 8));
-  l.total = up(l.norms + n_keys * 4);
+  l.partials = up(l.norms + n_keys * 4);
+  l.total = up(l.partials + static_cast<int64_t>(axr::score_error_partials(S)) * 8);
   return l;
 }
 
@@ -315,6 +316,7 @@ static int check_select_sizes(int S, int B, int Hq, int Hkv, int64_t T, int d, i
                               int dtype, int q_dtype) {
   static const uint32_t zero_signs[axr::kMaxSignWords] = {};
   if (S < 0) return fail(AXR_EINVAL, "S=%d is negative", S);
+  if (S > 64) return fail(AXR_EUNSUPPORTED, "S=%d calibration samples exceed 64", S);
   int rc = check_score_sizes(d, b, q_dtype, zero_signs, B, Hq, Hkv, T, T);
   if (rc != AXR_OK) return rc;
   if (!supported_dtype(dtype)) return fail(AXR_EUNSUPPORTED, "dtype=%d is not supported", dtype);
@@ -355,6 +357,7 @@ int axr_sign_selection_errors(const void* keys, int dtype, const void* q, int q_
   float* lut = reinterpret_cast<float*>(ws + lay.lut);
   uint32_t* packed = reinterpret_cast<uint32_t*>(ws + lay.packed);
   float* norms = reinterpret_cast<float*>(ws + lay.norms);
+  double* partials = reinterpret_cast<double*>(ws + lay.partials);
   const int rows = S * B;
   const int64_t n = static_cast<int64_t>(rows) * Hkv * T;
   int err = axr::launch_dense_scores(keys, dtype, q, q_dtype, rows, Hq, Hkv, T, d, exact, stream);
@@ -369,7 +372,7 @@ int axr_sign_selection_errors(const void* keys, int dtype, const void* q, int q_
     const axr::ScoreParams sp = score_params(sc, Hq, Hkv, T, T, d, b, nullptr);
     err = axr::launch_score(q, q_dtype, packed, norms, rows, d, b, sp, lut, stream);
     if (err != 0) return hip_status(err, "score kernel launch");
-    err = axr::launch_score_error(lut, exact, S, static_cast<int64_t>(B) * Hq * T,
+    err = axr::launch_score_error(lut, exact, S, static_cast<int64_t>(B) * Hq * T, partials,
                                   errors + static_cast<size_t>(c) * S * 2, stream);
     if (err != 0) return hip_status(err, "error kernel launch");
   }

@@ -82,8 +82,10 @@ int launch_softmax(float* scores, const float* partials, const int32_t* lens, in
 // (err[2i] = sum (lut - exact)^2, err[2i+1] = sum exact^2 over `per` scores).
 int launch_dense_scores(const void* keys, int kdt, const void* q, int qdt, int rows, int Hq,
                         int Hkv, int64_t T, int d, float* out, void* stream);
+// `part` is scratch of score_error_partials(samples) doubles.
+int score_error_partials(int samples);
 int launch_score_error(const float* lut, const float* exact, int samples, int64_t per,
-                       double* err, void* stream);
+                       double* part, double* err, void* stream);
 
 // Mode of the write kernel: quantize (indices + norms) or transform export.
 enum WriteMode { kWriteQuantize = 0, kWriteTransform = 1, kWriteTransformNormalized = 2 };

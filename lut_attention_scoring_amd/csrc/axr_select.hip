@@ -4,7 +4,8 @@
 // the sign pattern is chosen once, without gradients, among a few hundred
 // candidates on a few calibration samples.  For every candidate the host
 // runs the write and score kernels on the calibration keys; the kernels here
-// supply the exact scores to compare with and the per-sample error sums:
+// supply the exact scores to compare with and the per-sample error sums (in
+// two fixed-order fp64 passes):
 //   err[c][i] = sum (s_lut - s_exact)^2,  ref[c][i] = sum s_exact^2.
 
 #include <hip/hip_runtime.h>
@@ -64,16 +65,24 @@ __global__ __launch_bounds__(kDenseThreads) void dense_scores_kernel(
   }
 }
 
-constexpr int kErrThreads = 1024;
+constexpr int kErrThreads = 256;
+constexpr int kErrBlocks = 64;   // blocks per calibration sample
 
-// One block per calibration sample: fp64 sums of (lut - exact)^2 and
-// exact^2 over the sample's `per` scores, reduced in a fixed order.
-__global__ __launch_bounds__(kErrThreads) void score_error_kernel(
+// Block (i, j) sums (lut - exact)^2 and exact^2 over slice j of sample i's
+// `per` scores in fp64 and reduces them in a fixed order; the second kernel
+// adds the kErrBlocks partials of each sample in order, so the sums do not
+// depend on scheduling.
+__global__ __launch_bounds__(kErrThreads) void score_error_partial(
     const float* __restrict__ lut, const float* __restrict__ exact, int64_t per,
-    double* __restrict__ err) {
-  const size_t base = static_cast<size_t>(blockIdx.x) * per;
+    double* __restrict__ part) {
+  const int sample = blockIdx.x / kErrBlocks;
+  const int slice = blockIdx.x % kErrBlocks;
+  const int64_t chunk = (per + kErrBlocks - 1) / kErrBlocks;
+  const int64_t i0 = slice * chunk;
+  const int64_t i1 = i0 + chunk < per ? i0 + chunk : per;
+  const size_t base = static_cast<size_t>(sample) * per;
   double e = 0.0, r = 0.0;
-  for (int64_t i = threadIdx.x; i < per; i += kErrThreads) {
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += kErrThreads) {
     const double x = exact[base + i];
     const double dlt = static_cast<double>(lut[base + i]) - x;
     e = fma(dlt, dlt, e);
@@ -91,9 +100,22 @@ __global__ __launch_bounds__(kErrThreads) void score_error_kernel(
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    err[2 * blockIdx.x] = se[0];
-    err[2 * blockIdx.x + 1] = sr[0];
+    part[2 * blockIdx.x] = se[0];
+    part[2 * blockIdx.x + 1] = sr[0];
   }
+}
+
+__global__ __launch_bounds__(64) void score_error_final(const double* __restrict__ part,
+                                                       int samples, double* __restrict__ err) {
+  const int i = threadIdx.x;
+  if (i >= samples) return;
+  double e = 0.0, r = 0.0;
+  for (int j = 0; j < kErrBlocks; ++j) {
+    e += part[2 * (i * kErrBlocks + j)];
+    r += part[2 * (i * kErrBlocks + j) + 1];
+  }
+  err[2 * i] = e;
+  err[2 * i + 1] = r;
 }
 
 }  // namespace
@@ -115,11 +137,16 @@ int launch_dense_scores(const void* keys, int kdt, const void* q, int qdt, int r
   return static_cast<int>(hipGetLastError());
 }
 
+int score_error_partials(int samples) { return samples * kErrBlocks * 2; }
+
 int launch_score_error(const float* lut, const float* exact, int samples, int64_t per,
-                       double* err, void* stream) {
+                       double* part, double* err, void* stream) {
   if (samples == 0) return 0;
-  hipLaunchKernelGGL(score_error_kernel, dim3(samples), dim3(kErrThreads), 0,
-                     static_cast<hipStream_t>(stream), lut, exact, per, err);
+  if (samples > 64) return static_cast<int>(hipErrorInvalidValue);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(score_error_partial, dim3(samples * kErrBlocks), dim3(kErrThreads), 0, s,
+                     lut, exact, per, part);
+  hipLaunchKernelGGL(score_error_final, dim3(1), dim3(64), 0, s, part, samples, err);
   return static_cast<int>(hipGetLastError());
 }
 
