@@ -183,6 +183,8 @@ def main():
 
     append_ms = per_launch_ms(append, args.steps)
     decode_ms = per_launch_ms(decode_step, args.steps)
+    fused_ms = per_launch_ms(
+        lambda: axr.decode_step(q, new_k, bits, b, packed, norms, pos, out=scores), args.steps)
 
     # The same step captured once in a HIP graph and replayed (one launch
     # per step from the host).
@@ -337,9 +339,11 @@ def main():
                                "objective_chosen": float(sel_obj[sel_idx]),
                                "objective_worst": float(sel_obj.max())},
             "decode_step": {"ms": decode_ms, "graph_replay_ms": decode_graph_ms,
+                            "fused_ms": fused_ms,
                             "append_ms": append_ms,
                             "appended_keys": B * Hkv, "scored_keys": n,
-                            "note": "append one key per (sequence, KV head) + ragged score"},
+                            "note": "append one key per (sequence, KV head) + ragged score; "
+                                    "fused = one launch (axr_decode_step)"},
         },
     }
     if not args.no_cpu_baseline:

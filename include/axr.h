@@ -148,6 +148,26 @@ int axr_score_ragged(const void* q, int q_dtype, const uint32_t* packed, const f
                      int64_t T, int64_t t_cap, int d, int b, float* scores, void* stream);
 
 /*
+ * One decode step in one launch: the effect of axr_append_keys(k_new, pos)
+ * followed by axr_score_ragged(lens = pos + 1).  The block of the score
+ * kernel whose tile holds slot pos[bi] quantizes the new key itself (same
+ * rule as the write path; its arithmetic runs in a different order, so a
+ * coordinate within ~1e-7 of a threshold may take the neighbouring cell and
+ * the stored norm may differ in the last bits), stores its record and norm in
+ * the cache and scores it from the fresh record.
+ *   k_new : device [B][Hkv][d] of k_dtype, 4-byte aligned
+ *   pos   : device int32 [B]; a slot outside [0, t_cap) appends nothing and
+ *           row bi is scored for t < min(max(pos[bi] + 1, 0), T)
+ *   packed, norms : the cache, as for axr_append_keys (in/out)
+ *   scores: device float [B][Hq][T]; entries past a row's length are not written
+ * Same requirements and errors as axr_score.
+ */
+int axr_decode_step(const void* q, int q_dtype, const void* k_new, int k_dtype,
+                    const uint32_t* sign_bits, const int32_t* pos, int B, int Hq, int Hkv,
+                    int64_t T, int64_t t_cap, int d, int b, uint32_t* packed, float* norms,
+                    float* scores, void* stream);
+
+/*
  * Attention probabilities over the table-lookup scores, with the context split
  * across blocks.  The pages define the scores (AXELRAM, Abstract: score =
  * norm times the sum of table entries); the softmax over a row is the usual

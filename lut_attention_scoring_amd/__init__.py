@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "AxrError", "LIB_PATH", "lib", "version", "codebook", "sign_words",
-    "packed_words", "quantize_keys", "append_keys", "score", "score_softmax", "transform",
+    "packed_words", "quantize_keys", "append_keys", "decode_step", "score", "score_softmax",
+    "transform",
     "sign_selection_errors", "select_sign_pattern", "quantize_keys_isoquant",
     "transform_isoquant",
     "probe_read_stream",
@@ -83,6 +84,9 @@ def _load():
     so.axr_quantize_keys_isoquant.argtypes = [vp, i32, i64, i32, i32, vp, i32, vp, vp, vp]
     so.axr_transform_isoquant.restype = i32
     so.axr_transform_isoquant.argtypes = [vp, i32, i64, i32, vp, i32, i32, vp, vp]
+    so.axr_decode_step.restype = i32
+    so.axr_decode_step.argtypes = [vp, i32, vp, i32, u32p, vp, i32, i32, i32, i64, i64, i32, i32,
+                                   vp, vp, vp, vp]
     so.axr_transform.restype = i32
     so.axr_transform.argtypes = [vp, i32, i64, i32, u32p, i32, vp, vp]
     so.axr_probe_read_stream.restype = i32
@@ -186,6 +190,33 @@ def append_keys(keys: torch.Tensor, sign_bits, b: int, packed: torch.Tensor,
                                pos.data_ptr(), t_cap, packed.data_ptr(), norms.data_ptr(),
                                _stream(keys)))
     return packed, norms
+
+
+def decode_step(q: torch.Tensor, k_new: torch.Tensor, sign_bits, b: int, packed: torch.Tensor,
+                norms: torch.Tensor, pos: torch.Tensor, T: int = None, out: torch.Tensor = None):
+    """One decode step in one launch: k_new [B, Hkv, d] quantized into slot
+    pos[bi] of the cache and q [B, Hq, d] scored over t < pos[bi] + 1
+    -> scores fp32 [B, Hq, T] (T defaults to t_cap)."""
+    B, Hq, d = q.shape
+    Bc, Hkv, t_cap, W = packed.shape
+    if Bc != B or W != packed_words(d, b) or tuple(norms.shape) != (B, Hkv, t_cap):
+        raise ValueError("q, packed and norms shapes disagree")
+    if tuple(k_new.shape) != (B, Hkv, d):
+        raise ValueError("k_new must be [B, Hkv, d]")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (B,):
+        raise ValueError("pos must be an int32 tensor of shape [B]")
+    T = t_cap if T is None else int(T)
+    if out is None:
+        out = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    _need_cuda(q, k_new, packed, norms, pos, out)
+    if tuple(out.shape) != (B, Hq, T):
+        raise ValueError("out has the wrong shape")
+    words, wp = _words_ptr(sign_words(sign_bits))
+    _check(lib.axr_decode_step(q.data_ptr(), _dtype_code(q), k_new.data_ptr(),
+                               _dtype_code(k_new), wp, pos.data_ptr(), B, Hq, Hkv, T, t_cap, d,
+                               b, packed.data_ptr(), norms.data_ptr(), out.data_ptr(),
+                               _stream(q)))
+    return out
 
 
 def score(q: torch.Tensor, packed: torch.Tensor, norms: torch.Tensor, sign_bits, b: int,

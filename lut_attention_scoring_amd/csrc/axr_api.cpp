@@ -379,6 +379,33 @@ int axr_sign_selection_errors(const void* keys, int dtype, const void* q, int q_
   return ok();
 }
 
+int axr_decode_step(const void* q, int q_dtype, const void* k_new, int k_dtype,
+                    const uint32_t* sign_bits, const int32_t* pos, int B, int Hq, int Hkv,
+                    int64_t T, int64_t t_cap, int d, int b, uint32_t* packed, float* norms,
+                    float* scores, void* stream) {
+  int rc = check_score_sizes(d, b, q_dtype, sign_bits, B, Hq, Hkv, T, t_cap);
+  if (rc != AXR_OK) return rc;
+  if (!supported_dtype(k_dtype)) return fail(AXR_EUNSUPPORTED, "k_dtype=%d is not supported", k_dtype);
+  if (B == 0 || T == 0) return ok();
+  if (q == nullptr || k_new == nullptr || pos == nullptr || packed == nullptr ||
+      norms == nullptr || scores == nullptr)
+    return fail(AXR_EINVAL, "q, k_new, pos, packed, norms and scores must be non-null");
+  if (!aligned(q, 16) || !aligned(packed, 16))
+    return fail(AXR_EALIGN, "q and packed must be 16-byte aligned");
+  if (!aligned(k_new, 4) || !aligned(pos, 4) || !aligned(norms, 4) || !aligned(scores, 4))
+    return fail(AXR_EALIGN, "k_new, pos, norms and scores must be 4-byte aligned");
+  axr::ScoreParams p = score_params(sign_bits, Hq, Hkv, T, t_cap, d, b, nullptr);
+  p.knew = k_new;
+  p.kdt = k_dtype;
+  p.pos = pos;
+  p.packed_out = packed;
+  p.norms_out = norms;
+  const axr::WriteParams wp = write_params(sign_bits, d, b);
+  for (int i = 0; i < axr::kMaxLevels / 2; ++i) p.tpos[i] = wp.tpos[i];
+  int err = axr::launch_score(q, q_dtype, packed, norms, B, d, b, p, scores, stream);
+  return hip_status(err, "score kernel launch");
+}
+
 int axr_score_ragged(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
                      const uint32_t* sign_bits, int B, int Hq, int Hkv, const int32_t* lens,
                      int64_t T, int64_t t_cap, int d, int b, float* scores, void* stream) {

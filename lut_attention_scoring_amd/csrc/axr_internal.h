@@ -59,6 +59,16 @@ struct ScoreParams {
   // exp(scale * score - m); (-inf, 0) for a tile with no tokens.
   float* partials;
   float scale;
+  // Optional fused decode step (knew != nullptr): the new key knew[bi][kvh]
+  // (dtype kdt) is quantized with the write path's rule into slot pos[bi] of
+  // the cache (stored by the first head group's block) and row bi is scored
+  // for t < pos[bi] + 1 with that record in place.
+  const void* knew;
+  int kdt;
+  const int32_t* pos;
+  uint32_t* packed_out;           // the cache (same buffers as packed / norms)
+  float* norms_out;
+  float tpos[kMaxLevels / 2];     // positive thresholds times sqrt(d)
 };
 
 // Launchers (return a hipError_t value as int; 0 = success).

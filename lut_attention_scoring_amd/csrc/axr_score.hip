@@ -92,6 +92,38 @@ __device__ __forceinline__ void qlane_stage(float (&v)[R], int lane) {
   for (int r = 0; r < R; ++r) v[r] = fmaf(v[r], sgn, lane_xor<M>(v[r]));
 }
 
+// Walsh-Hadamard transform (no scale) of a row spread over a wave, lane l
+// holding coordinates l + 64 r: butterflies over r in registers, then over
+// the lane bits by cross-lane exchange.
+template <int R>
+__device__ __forceinline__ void wht_row(float (&v)[R], int lane) {
+#pragma unroll
+  for (int h = 1; h < R; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+  qlane_stage<1>(v, lane);
+  qlane_stage<2>(v, lane);
+  qlane_stage<4>(v, lane);
+  qlane_stage<8>(v, lane);
+  qlane_stage<16>(v, lane);
+  qlane_stage<32>(v, lane);
+}
+
+// Element r of a row stored as fp32, fp16 or bf16, at lane + 64 r.
+__device__ __forceinline__ float row_elem(const void* p, int dtype, size_t i) {
+  if (dtype == AXR_F32) return static_cast<const float*>(p)[i];
+  const uint16_t h = static_cast<const uint16_t*>(p)[i];
+  if (dtype == AXR_F16) return __half2float(__ushort_as_half(h));
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
 template <int D, int BITS, int P>
 struct ScoreShape {
   static constexpr int LPK = D / 32;            // lanes per key
@@ -161,7 +193,11 @@ __device__ __forceinline__ void buffer_load_words(uint32_t (&dst)[WL], __amdgpu_
   }
 }
 
-template <int D, int BITS, int P, int NT, int NTHREADS>
+// What a launch computes besides the scores: nothing, the split-T softmax
+// partials, or the fused decode step's new key.
+enum ScoreMode { kPlain = 0, kLse = 1, kDecode = 2 };
+
+template <int D, int BITS, int P, int NT, int NTHREADS, int MODE>
 __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict__ q, int qdt,
                                                        const uint32_t* __restrict__ packed,
                                                        const float* __restrict__ norms,
@@ -191,15 +227,21 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   const int kw = lane / S::LPK;                 // key index in the wave
   constexpr int KPB = (NTHREADS / 64) * S::KPW;  // keys per block iteration
   constexpr uint32_t REC_BYTES = S::W * 4;
-  // tokens [0, len) of this batch row are scored: T, or lens[bi] (clamped)
+  // tokens [0, len) of this batch row are scored: T, or lens[bi] (clamped),
+  // or pos[bi] + 1 in a fused decode step
   int64_t len = prm.T;
-  if (prm.lens != nullptr) {
+  int64_t slot = -1;                            // the decode step's new token
+  if constexpr (MODE == kDecode) {
+    slot = prm.pos[bi];
+    const int64_t l = slot + 1;
+    len = l < 0 ? 0 : (l < prm.T ? l : prm.T);
+  } else if (prm.lens != nullptr) {
     const int64_t l = prm.lens[bi];
     len = l < 0 ? 0 : (l < prm.T ? l : prm.T);
   }
   const int64_t t0 = static_cast<int64_t>(tile) * prm.tile_len;
   if (t0 >= len) {                              // block-uniform: nothing to score
-    if (prm.partials != nullptr && tid < nvalid) {
+    if (MODE == kLse && tid < nvalid) {
       float* part = prm.partials + ((static_cast<size_t>(bi) * prm.Hq + h0 + tid) * prm.tiles + tile) * 2;
       part[0] = -INFINITY;
       part[1] = 0.0f;
@@ -208,6 +250,11 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   }
   const int64_t t1 = (t0 + prm.tile_len < len) ? t0 + prm.tile_len : len;
   const size_t rowbase = static_cast<size_t>(row) * prm.t_cap;
+  // block-uniform: this tile holds the decode step's new token
+  const bool holds_new = MODE == kDecode && slot >= t0 && slot < t1;
+  __shared__ uint8_t nidx[D];                   // its indices, then its record
+  __shared__ uint32_t newrec[S::W];
+  __shared__ float newnrm;
 
   // Records and norms of this (batch, KV head) row through raw buffer
   // resources that end at this block's last token: loads past the tile return
@@ -268,23 +315,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 
   if (wave < GB) {
     const int g = wave;
-#pragma unroll
-    for (int h = 1; h < R; h <<= 1) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        if ((i & h) == 0) {
-          const float a = v[i], b = v[i + h];
-          v[i] = a + b;
-          v[i + h] = a - b;
-        }
-      }
-    }
-    qlane_stage<1>(v, lane);
-    qlane_stage<2>(v, lane);
-    qlane_stage<4>(v, lane);
-    qlane_stage<8>(v, lane);
-    qlane_stage<16>(v, lane);
-    qlane_stage<32>(v, lane);
+    wht_row<R>(v, lane);
     const float inv_sqrt_d = 1.0f / sqrtf(static_cast<float>(D));
     float sa = 0.0f;
 #pragma unroll
@@ -310,7 +341,59 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
       hinv[g] = ldexpf(1.0f, -sh);
     }
   }
+  // Fused decode step: one wave quantizes the new key with the write path's
+  // rule (sign pattern, Walsh-Hadamard transform, index = number of
+  // thresholds below z, a zero key in the cell below 0), lane l holding
+  // coordinates l + 64 r; indices go to LDS for packing below.
+  if (MODE == kDecode && holds_new && wave == NTHREADS / 64 - 1) {
+    const size_t krow = (static_cast<size_t>(bi) * prm.Hkv + kvh) * D + lane;
+    float kv[R];
+    float ss = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float x = row_elem(prm.knew, prm.kdt, krow + 64 * r);
+      ss = fmaf(x, x, ss);
+      const uint32_t s_lo = __builtin_amdgcn_readfirstlane(prm.sign[2 * r]);
+      const uint32_t s_hi = __builtin_amdgcn_readfirstlane(prm.sign[2 * r + 1]);
+      const uint32_t sw = (lane & 32) ? s_hi : s_lo;
+      kv[r] = __uint_as_float(__float_as_uint(x) ^ (((sw >> (lane & 31)) & 1u) << 31));
+    }
+    ss += lane_xor<1>(ss);
+    ss += lane_xor<2>(ss);
+    ss += lane_xor<4>(ss);
+    ss += lane_xor<8>(ss);
+    ss += lane_xor<16>(ss);
+    ss += lane_xor<32>(ss);
+    const float nrm = sqrtf(ss);
+    wht_row<R>(kv, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float a = fabsf(kv[r]);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i + 1 < HL; ++i) cnt += a > prm.tpos[i] * nrm ? 1 : 0;
+      nidx[lane + 64 * r] = static_cast<uint8_t>(kv[r] > 0.0f ? HL + cnt : HL - 1 - cnt);
+    }
+    if (lane == 0) newnrm = nrm;
+  }
   __syncthreads();
+
+  // ... and packs them into the record: thread i of the last wave assembles
+  // word i; the first head group's block also stores record and norm.
+  if (MODE == kDecode && holds_new && tid >= NTHREADS - S::W) {
+    const int wi = tid - (NTHREADS - S::W);
+    uint32_t word = 0u;
+    for (int j = (32 * wi) / BITS; j <= (32 * wi + 31) / BITS && j < D; ++j) {
+      const int sh = BITS * j - 32 * wi;
+      const uint32_t v = nidx[j];
+      word |= sh >= 0 ? v << sh : v >> (-sh);
+    }
+    newrec[wi] = word;
+    if (hg == 0) {
+      prm.packed_out[(rowbase + static_cast<size_t>(slot)) * S::W + wi] = word;
+      if (wi == 0) prm.norms_out[rowbase + static_cast<size_t>(slot)] = newnrm;
+    }
+  }
 
   // Issue the first PD batches of record loads now: after the query loads
   // (which start the critical path and should not queue behind them) and
@@ -405,7 +488,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   // softmax partials of the heads this lane stores: with four lanes per key
   // heads 4 * k + u (k < NT), otherwise head u
   constexpr int NSLOT = S::LPK == 4 ? NT : 1;
-  const bool want_lse = prm.partials != nullptr;
+  constexpr bool want_lse = MODE == kLse;
   const float lse_scale = prm.scale;
   float sm_m[NSLOT], sm_l[NSLOT];
 #pragma unroll
@@ -427,6 +510,14 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 #pragma unroll
         for (int i = 0; i < S::WL; ++i) w[il][i] = wq[pd][i];
         nk[il] = nq[pd];
+        if (MODE == kDecode && holds_new) {
+          // the new token's record comes from LDS, not from the cache
+          if (tb0 + static_cast<int64_t>(pd) * KPB + kw == slot) {
+#pragma unroll
+            for (int i = 0; i < S::WL; ++i) w[il][i] = newrec[u * S::WL + i];
+            nk[il] = newnrm;
+          }
+        }
         const uint32_t sb =
             static_cast<uint32_t>(tb0 - tw) + static_cast<uint32_t>(pd + PD) * KPB;
         buffer_load_words<S::WL>(wq[pd], rrec, vrec, sb * REC_BYTES);
@@ -502,7 +593,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 
   // Split-T softmax partials of this tile: merge the lanes that hold the same
   // head (lane bits above the key's LPK lanes), then the waves, through LDS.
-  if (want_lse) {
+  if constexpr (want_lse) {
     __shared__ float red[NTHREADS / 64][GB][2];
 #pragma unroll
     for (int k = 0; k < NSLOT; ++k) {
@@ -556,7 +647,10 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
   p.heads_per_block = 4 * NT;
   p.head_groups = (p.G + 4 * NT - 1) / (4 * NT);
   const int64_t rows = static_cast<int64_t>(B) * p.Hkv * p.head_groups;
-  const int64_t per_cu = bytes <= 80 * 1024 ? 2 : 1;
+  const int mode = p.knew != nullptr ? kDecode : (p.partials != nullptr ? kLse : kPlain);
+  // two blocks per CU when the LDS allows (the decode-step instance needs
+  // more registers than two 1024-thread blocks can hold)
+  const int64_t per_cu = bytes <= 80 * 1024 && mode != kDecode ? 2 : 1;
   const int64_t target = 256 * per_cu;          // one wave of resident blocks
   int64_t tiles = (target + rows - 1) / rows;
   int64_t tile_len = (p.T + tiles - 1) / tiles;
@@ -571,8 +665,17 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
     *plan = p;
     return 0;
   }
-  hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS>), dim3(static_cast<unsigned>(grid)),
-                     dim3(NTHREADS), 0, s, q, qdt, packed, norms, scores, p);
+  const dim3 g(static_cast<unsigned>(grid)), blk(NTHREADS);
+  if (mode == kDecode) {
+    hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kDecode>), g, blk, 0, s, q, qdt,
+                       packed, norms, scores, p);
+  } else if (mode == kLse) {
+    hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kLse>), g, blk, 0, s, q, qdt,
+                       packed, norms, scores, p);
+  } else {
+    hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kPlain>), g, blk, 0, s, q, qdt,
+                       packed, norms, scores, p);
+  }
   return static_cast<int>(hipGetLastError());
 }
 

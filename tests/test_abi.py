@@ -234,3 +234,20 @@ def test_sign_selection_validation():
     assert sel(ws=FAKE + 16)[0] == axr.EALIGN
     assert sel(errors=FAKE + 4)[0] == axr.EALIGN
     assert sel(C=0, keys=None, cand=None, errors=None, ws=None)[0] == axr.OK
+
+
+def test_decode_step_validation():
+    f = axr.lib.axr_decode_step
+
+    def ds(q=FAKE, kdt=axr.F16, k=FAKE, pos=FAKE, packed=FAKE, norms=FAKE, scores=FAKE, B=2,
+           T=64, t_cap=64):
+        return _status(f, q, axr.F16, k, kdt, SIGNS, pos, B, 8, 2, T, t_cap, 128, 3, packed, norms,
+                       scores, None)
+    assert ds(kdt=7)[0] == axr.EUNSUPPORTED
+    assert ds(k=None)[0] == axr.EINVAL
+    assert ds(pos=None)[0] == axr.EINVAL
+    assert ds(packed=None)[0] == axr.EINVAL
+    assert ds(t_cap=10)[0] == axr.EINVAL
+    assert ds(k=FAKE + 2)[0] == axr.EALIGN
+    assert ds(packed=FAKE + 8)[0] == axr.EALIGN
+    assert ds(B=0, q=None, k=None, pos=None, packed=None, norms=None, scores=None)[0] == axr.OK

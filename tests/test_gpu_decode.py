@@ -235,3 +235,78 @@ def test_decode_step_llama_full_size_sampled():
                       f"llama decode bi={bi}")
         after = f64(out[bi, :, n_tok:])
         assert np.all(after == SENTINEL)
+
+
+# ---------------------------------------------------------------------------
+# The fused decode step (axr_decode_step): append and score in one launch.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,b,G,dtype", [
+    (128, 3, 4, torch.float16), (128, 2, 1, torch.float32), (128, 4, 8, torch.bfloat16),
+    (128, 3, 16, torch.float16), (256, 3, 8, torch.float16), (512, 4, 4, torch.bfloat16),
+    (512, 2, 8, torch.float32)])
+def test_fused_decode_step(d, b, G, dtype):
+    m = axr()
+    rng = np.random.default_rng(5000 + d + 10 * b + G)
+    Hkv, t_cap, T = 2, 2100, 2000
+    pos = [0, 1999, 777, -1, 2050, 255, 256, 1023]        # tile edges, -1, past T, past t_cap
+    pos[4] = t_cap + 3
+    B = len(pos)
+    bits = W.sign_bits(d)
+    cache = _keys(rng, (B, Hkv, t_cap, d), dtype)
+    packed, norms = m.quantize_keys(cache.to(DEV), bits, b)
+    new = _keys(rng, (B, Hkv, d), dtype, scale=4.0)
+    q = _keys(rng, (B, Hkv * G, d), dtype, scale=1.0)
+    out = torch.full((B, Hkv * G, T), SENTINEL, device=DEV)
+    torch.cuda.synchronize()
+    before_p, before_n = words_u32(packed).copy(), norms.cpu().numpy().copy()
+    m.decode_step(q.to(DEV), new.to(DEV), bits, b, packed, norms,
+                  torch.tensor(pos, dtype=torch.int32, device=DEV), T=T, out=out)
+    torch.cuda.synchronize()
+    label = f"fused d={d} b={b} G={G}"
+    # appended records against the oracle's write of the new keys; all else untouched
+    assert _check_appended(new, packed, norms, pos, bits, b, label) == 6
+    _untouched(before_p, before_n, words_u32(packed), norms.cpu().numpy(), pos)
+    # scores given the GPU's (new) records
+    keys_now = cache.clone()
+    for bi, slot in enumerate(pos):
+        if 0 <= slot < t_cap:
+            keys_now[bi, :, slot] = new[bi]
+    s = A.signs_from_bits(bits)
+    c, _ = A.lloyd_max_codebook(d, b)
+    qprime = A.transform_queries(f64(q), s)
+    got = f64(out)
+    for bi, slot in enumerate(pos):
+        n_tok = min(max(slot + 1, 0), T)
+        assert np.all(got[bi, :, n_tok:] == SENTINEL), f"{label} bi={bi} wrote past its length"
+        if n_tok == 0:
+            continue
+        toks = np.unique(np.concatenate([np.arange(0, n_tok, 37), [n_tok - 1]]))
+        tt = torch.from_numpy(toks)
+        gidx = A.unpack_indices(words_u32(packed[bi:bi + 1, :, tt]), d, b)
+        onorm = A.key_norms(f64(keys_now[bi:bi + 1, :, tt]))
+        assert_scores(got[bi:bi + 1, :, toks], qprime[bi:bi + 1], gidx, onorm, c,
+                      f"{label} bi={bi}")
+
+
+def test_fused_decode_step_matches_two_launches():
+    """Fused and two-launch decode steps agree: records within the boundary
+    rule (checked above), scores of every other token bit for bit, and the
+    new token's score within the score bound."""
+    m = axr()
+    rng = np.random.default_rng(61)
+    d, b, B, Hkv, G, t_cap = 128, 3, 4, 2, 4, 3000
+    bits = W.sign_bits(d)
+    cache = _keys(rng, (B, Hkv, t_cap, d), torch.float16).to(DEV)
+    p1, n1 = m.quantize_keys(cache, bits, b)
+    p2, n2 = p1.clone(), n1.clone()
+    new = _keys(rng, (B, Hkv, d), torch.float16).to(DEV)
+    q = _keys(rng, (B, Hkv * G, d), torch.float16, scale=1.0).to(DEV)
+    pos = torch.tensor([2999, 100, 1500, 4095 % 3000], dtype=torch.int32, device=DEV)
+    fused = m.decode_step(q, new, bits, b, p1, n1, pos)
+    m.append_keys(new, bits, b, p2, n2, pos)
+    two = m.score(q, p2, n2, bits, b, lens=pos + 1)
+    torch.cuda.synchronize()
+    for bi, slot in enumerate(pos.tolist()):
+        assert torch.equal(fused[bi, :, :slot], two[bi, :, :slot])
+    torch.testing.assert_close(n1, n2, rtol=1e-6, atol=0)
