@@ -33,12 +33,12 @@ CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
 # runs.  Valid only for the kernel sources they were taken on (SHA-1 of the
 # files below); otherwise traffic is reported as null.
 COUNTER_TRAFFIC = {
-    "write": {"sources": ["axr_write.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "ec5941c7bd91cae2728afba258fae5e71881a915",
-              "bytes": (262222.0 * 2.0 + 107143.9) * 1024},
+    "write": {"sources": ["axr_write.hip", "axr_keyquant.h", "axr_device.h", "axr_internal.h"],
+              "sha1": "b09a3fff888a695c0ebd6b23e9eea6617786dcf4",
+              "bytes": (262203.5 * 2.0 + 107146.5) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "6213716b7b03762e7d18bda09fe12cb808d3174c",
-              "bytes": (53565.2 * 2.0 + 32792.1) * 1024},
+              "sha1": "0ead9d53d40a4bd8b534cbeba873053dfdb38749",
+              "bytes": (53548.4 * 2.0 + 32776.8) * 1024},
 }
 
 
