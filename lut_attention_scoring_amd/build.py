@@ -24,6 +24,10 @@ HIPCC_FLAGS = [
     "-shared",
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # The score kernel's work counter is bumped by one lane per wave and its
+    # result is read a step later; the atomic optimizer would rewrite the
+    # bump as a wave-wide scan that waits for the result at once.
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall",
 ]
 

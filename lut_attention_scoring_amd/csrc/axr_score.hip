@@ -225,7 +225,6 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   const int wave = tid / 64, lane = tid % 64;
   const int u = lane % S::LPK;                  // 32-coordinate chunk of the key
   const int kw = lane / S::LPK;                 // key index in the wave
-  constexpr int KPB = (NTHREADS / 64) * S::KPW;  // keys per block iteration
   constexpr uint32_t REC_BYTES = S::W * 4;
   // tokens [0, len) of this batch row are scored: T, or lens[bi] (clamped),
   // or pos[bi] + 1 in a fused decode step
@@ -266,9 +265,20 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   const __amdgpu_buffer_rsrc_t rnrm = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(norms + rowbase), 0, static_cast<int>(static_cast<uint32_t>(t1) * 4u),
       kRsrcWord3);
-  const int64_t tw = t0 + wave * S::KPW;        // first token of this wave's first batch
-  const uint32_t vrec = static_cast<uint32_t>(tw + kw) * REC_BYTES + u * (S::WL * 4);
-  const uint32_t vnrm = static_cast<uint32_t>(tw + kw) * 4u;
+  // The tile is cut into units of S::KPW tokens, one per wave per batch:
+  // unit k holds tokens t0 + k KPW + [0, KPW).  Each wave's first PD units
+  // are fixed (the block's first PD batches, wave-interleaved); the rest come
+  // from an LDS counter, IL at a time, so the waves that the issue
+  // arbitration favours take more of them and all waves end together.  Unit
+  // offsets go into the vector offset, which the buffer range check covers.
+  constexpr int NW = NTHREADS / 64;
+  const uint32_t wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t tile_keys = static_cast<uint32_t>(t1 - t0);
+  const uint32_t units = (tile_keys + S::KPW - 1) / S::KPW;
+  __shared__ uint32_t next_unit;
+  if (tid == 0) next_unit = PD * NW;
+  const uint32_t vrec = static_cast<uint32_t>(t0 + kw) * REC_BYTES + u * (S::WL * 4);
+  const uint32_t vnrm = static_cast<uint32_t>(t0 + kw) * 4u;
 
   // 1. q' = H (s * q) / sqrt(d) for head g by wave g, in registers: lane l
   //    holds coordinates l + 64 r; butterflies over r in registers and over
@@ -400,11 +410,13 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   // before the table build, which they overlap.
   uint32_t wq[PD][S::WL];
   float nq[PD];
+  uint32_t ks[PD];                              // unit of each batch in flight
 #pragma unroll
   for (int pd = 0; pd < PD; ++pd) {
-    buffer_load_words<S::WL>(wq[pd], rrec, vrec, pd * KPB * REC_BYTES);
+    ks[pd] = static_cast<uint32_t>(pd * NW) + wave_s;
+    buffer_load_words<S::WL>(wq[pd], rrec, vrec + ks[pd] * (S::KPW * REC_BYTES), 0);
     nq[pd] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           rnrm, vnrm, pd * KPB * 4u, 0));
+                                           rnrm, vnrm + ks[pd] * (S::KPW * 4u), 0, 0));
   }
 
   // 2. the tables, one 16-byte entry (4 heads) per (lane chunk u, group v,
@@ -472,9 +484,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 #pragma unroll
   for (int t4 = 0; t4 < NT; ++t4) {
     const uint32_t g = static_cast<uint32_t>((4 * t4 + u) % GB);
-    vsc[t4] = (g * static_cast<uint32_t>(prm.T) + static_cast<uint32_t>(tw + kw)) * 4u;
+    vsc[t4] = (g * static_cast<uint32_t>(prm.T) + static_cast<uint32_t>(t0 + kw)) * 4u;
   }
-  const uint32_t tile_keys = static_cast<uint32_t>(t1 - tw);  // this wave's tokens past tw
   __syncthreads();
   float ginv[GB];                               // 2^-e per head
 #pragma unroll
@@ -482,9 +493,9 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 #pragma unroll
   for (int t4 = 0; t4 < NT; ++t4) ginv_u[t4] = hinv[(4 * t4 + u) % GB];
 
-  // 3. stream the tile, keeping PD batches of records in flight and working
+  // 3. stream the tile, keeping PD units of records in flight and working
   //    on IL of them at once (independent lookups interleave in the LDS
-  //    queue).  A batch past the tile end is computed but not stored.
+  //    queue).  A unit past the tile end is computed but not stored.
   // softmax partials of the heads this lane stores: with four lanes per key
   // heads 4 * k + u (k < NT), otherwise head u
   constexpr int NSLOT = S::LPK == 4 ? NT : 1;
@@ -498,31 +509,42 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   }
 
   const char* lut_bytes = reinterpret_cast<const char*>(lut);
-  for (int64_t tb0 = tw; tb0 < t1; tb0 += PD * KPB) {
+  // the next IL units, taken one step before they are needed so that the
+  // counter's round trip overlaps the lookups; a wave leaves at its first
+  // unit past the tile, and every unit it took later lies past it too
+  uint32_t grab = 0u;
+  if (lane == 0) grab = atomicAdd(&next_unit, static_cast<uint32_t>(IL));
+  for (bool more = true; more;) {
 #pragma unroll
     for (int pd0 = 0; pd0 < PD; pd0 += IL) {
-      if (tb0 + static_cast<int64_t>(pd0) * KPB >= t1) break;   // wave-uniform
+      if (ks[pd0] >= units) {                   // wave-uniform
+        more = false;
+        break;
+      }
+      const uint32_t kn = __builtin_amdgcn_readfirstlane(grab);
+      if (lane == 0) grab = atomicAdd(&next_unit, static_cast<uint32_t>(IL));
       uint32_t w[IL][S::WL];
       float nk[IL];
+      uint32_t kc[IL];
 #pragma unroll
       for (int il = 0; il < IL; ++il) {
         const int pd = pd0 + il;
 #pragma unroll
         for (int i = 0; i < S::WL; ++i) w[il][i] = wq[pd][i];
         nk[il] = nq[pd];
+        kc[il] = ks[pd];
         if (MODE == kDecode && holds_new) {
           // the new token's record comes from LDS, not from the cache
-          if (tb0 + static_cast<int64_t>(pd) * KPB + kw == slot) {
+          if (t0 + static_cast<int64_t>(kc[il]) * S::KPW + kw == slot) {
 #pragma unroll
             for (int i = 0; i < S::WL; ++i) w[il][i] = newrec[u * S::WL + i];
             nk[il] = newnrm;
           }
         }
-        const uint32_t sb =
-            static_cast<uint32_t>(tb0 - tw) + static_cast<uint32_t>(pd + PD) * KPB;
-        buffer_load_words<S::WL>(wq[pd], rrec, vrec, sb * REC_BYTES);
+        ks[pd] = kn + il;
+        buffer_load_words<S::WL>(wq[pd], rrec, vrec + ks[pd] * (S::KPW * REC_BYTES), 0);
         nq[pd] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                               rnrm, vnrm, sb * 4u, 0));
+                                               rnrm, vnrm + ks[pd] * (S::KPW * 4u), 0, 0));
         rotate_right<S::WL>(w[il], rot);
       }
 
@@ -549,8 +571,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
       }
 #pragma unroll
       for (int il = 0; il < IL; ++il) {
-        const int64_t t = tb0 + static_cast<int64_t>(pd0 + il) * KPB + kw;
-        const uint32_t tb_rel = static_cast<uint32_t>(tb0 - tw) + (pd0 + il) * KPB;
+        const uint32_t tb_rel = kc[il] * S::KPW;  // the unit's first token past t0
+        const int64_t t = t0 + tb_rel + kw;
         const bool valid = tb_rel + kw < tile_keys;
         if constexpr (S::LPK == 4) {
           // lane u of the key ends with head u (and u + 4 when NT = 2)
@@ -638,8 +660,8 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
   constexpr int tbytes = table_bytes<D, BITS, P>(NT);
   constexpr int bytes = tbytes + 4 * NT * D * 4 + 2 * 4 * NT * 4;  // + q' + scales
   static_assert(tbytes <= kLdsBudget, "table exceeds the LDS budget");
-  // 1024-thread blocks (two fit per CU below 76 KiB of tables), except the
-  // single-coordinate two-table case whose registers need 512-thread blocks.
+  // 1024-thread blocks, except the single-coordinate two-table case whose
+  // registers need 512-thread blocks.
   constexpr int NTHREADS = (P == 1 && NT == 2) ? 512 : 1024;
   static_assert(bytes <= 160 * 1024, "LDS per block exceeded");
   using S = ScoreShape<D, BITS, P>;
@@ -648,10 +670,10 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
   p.head_groups = (p.G + 4 * NT - 1) / (4 * NT);
   const int64_t rows = static_cast<int64_t>(B) * p.Hkv * p.head_groups;
   const int mode = p.knew != nullptr ? kDecode : (p.partials != nullptr ? kLse : kPlain);
-  // two blocks per CU when the LDS allows (the decode-step instance needs
-  // more registers than two 1024-thread blocks can hold)
-  const int64_t per_cu = bytes <= 80 * 1024 && mode != kDecode ? 2 : 1;
-  const int64_t target = 256 * per_cu;          // one wave of resident blocks
+  // One block per CU, each with one tile: a second resident block would
+  // halve the tile over which the table build is spread, and the loop is
+  // issue-bound either way.
+  const int64_t target = 256;
   int64_t tiles = (target + rows - 1) / rows;
   int64_t tile_len = (p.T + tiles - 1) / tiles;
   if (tile_len < 4 * KPB) tile_len = 4 * KPB;   // amortise the table build
