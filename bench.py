@@ -37,8 +37,8 @@ COUNTER_TRAFFIC = {
               "sha1": "b09a3fff888a695c0ebd6b23e9eea6617786dcf4",
               "bytes": (262203.5 * 2.0 + 107146.5) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "0ead9d53d40a4bd8b534cbeba873053dfdb38749",
-              "bytes": (53548.4 * 2.0 + 32776.8) * 1024},
+              "sha1": "435ee0628b394fe7c04c0688888feb235f74fd12",
+              "bytes": (53433.2 * 2.0 + 34827.3) * 1024},
 }
 
 

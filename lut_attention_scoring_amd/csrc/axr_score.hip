@@ -138,8 +138,7 @@ struct ScoreShape {
   static constexpr int TBYTES = 256 * LPK * ROWS_U;  // bytes per 4-head table
 };
 
-constexpr int PD = 2;                // record batches in flight per wave
-constexpr int IL = 1;                // batches processed together
+constexpr int IL = 1;                // record units processed together
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit dword format
 
 // (field << 8) for the width-bit field at bit pos of an N-word bit string,
@@ -226,6 +225,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   const int u = lane % S::LPK;                  // 32-coordinate chunk of the key
   const int kw = lane / S::LPK;                 // key index in the wave
   constexpr uint32_t REC_BYTES = S::W * 4;
+  constexpr int CH = 8 / NT < S::NV ? 8 / NT : S::NV;  // steps per batch of lookups
+  constexpr int PD = NT == 1 ? 3 : 2;           // record units in flight per wave
   // tokens [0, len) of this batch row are scored: T, or lens[bi] (clamped),
   // or pos[bi] + 1 in a fused decode step
   int64_t len = prm.T;
@@ -429,35 +430,46 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
       return 16 * (uu * S::ROWS_U + (vv / 16) * S::NE + ff) + ((vv + S::KPG * uu) & 15);
     };
     constexpr int HALF_NE = S::NE / 2;           // fields with the top bit clear
-    constexpr int TASKS = NT * S::LPK * S::NV * HALF_NE;
-    // group index fastest: the 16 lanes of a quarter-wave write 16 distinct
-    // LDS columns
-    for (int task = tid; task < TASKS; task += NTHREADS) {
-      const int vv = task % S::NV;
-      const int f = (task / S::NV) % HALF_NE;
-      const int uu = (task / (HALF_NE * S::NV)) % S::LPK;
-      const int t4 = task / (HALF_NE * S::NV * S::LPK);
+    constexpr int GROUPS = NT * S::LPK * S::NV;  // (table, chunk, group) triples
+    // FSPLIT threads share a triple, each taking every FSPLIT-th field, so a
+    // thread reads its coordinates and head scales once.  Triple index
+    // fastest: the 16 lanes of a quarter-wave write 16 distinct LDS columns.
+    constexpr int FSPLIT = NTHREADS / GROUPS < 1 ? 1
+                           : (NTHREADS / GROUPS < HALF_NE ? NTHREADS / GROUPS : HALF_NE);
+    for (int item = tid; item < GROUPS * FSPLIT; item += NTHREADS) {
+      const int vv = item % S::NV;
+      const int uu = (item / S::NV) % S::LPK;
+      const int t4 = (item / (S::NV * S::LPK)) % NT;
+      const int f0 = item / GROUPS;
       const int j = 32 * uu + P * vv;
       int4* tab = lut + t4 * (S::TBYTES / 16);
-      int e[4];
+      // q'_j 2^e (exact: the scale is a power of two) for the four heads
+      float qa[4], qb[4];
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) {
         const int g = 4 * t4 + hh;
-        const float sc = hscale[g];
-        if constexpr (P == 1) {
-          e[hh] = __float2int_rn(qs[g][j] * cent[f] * sc);
-        } else {
-          e[hh] = __float2int_rn(qs[g][j] * cent[f & (L - 1)] * sc) +
-                  __float2int_rn(qs[g][j + 1] * cent[f >> BITS] * sc);
-        }
+        qa[hh] = qs[g][j] * hscale[g];
+        qb[hh] = P == 2 ? qs[g][j + P - 1] * hscale[g] : 0.0f;
       }
-      const int fm = (S::NE - 1) ^ f;            // every field mirrored
-      // With four lanes per key, component i of chunk u's entries holds head
-      // u ^ i (see quad_reduce_scatter); otherwise heads are in order.
-      const int pu = S::LPK == 4 ? (uu & 3) : 0;
-      const int c0 = e[0 ^ pu], c1 = e[1 ^ pu], c2 = e[2 ^ pu], c3 = e[3 ^ pu];
-      tab[slot_of(uu, vv, f)] = make_int4(c0, c1, c2, c3);
-      tab[slot_of(uu, vv, fm)] = make_int4(-c0, -c1, -c2, -c3);
+      for (int f = f0; f < HALF_NE; f += FSPLIT) {
+        int e[4];
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+          if constexpr (P == 1) {
+            e[hh] = __float2int_rn(qa[hh] * cent[f]);
+          } else {
+            e[hh] = __float2int_rn(qa[hh] * cent[f & (L - 1)]) +
+                    __float2int_rn(qb[hh] * cent[f >> BITS]);
+          }
+        }
+        const int fm = (S::NE - 1) ^ f;            // every field mirrored
+        // With four lanes per key, component i of chunk u's entries holds head
+        // u ^ i (see quad_reduce_scatter); otherwise heads are in order.
+        const int pu = S::LPK == 4 ? (uu & 3) : 0;
+        const int c0 = e[0 ^ pu], c1 = e[1 ^ pu], c2 = e[2 ^ pu], c3 = e[3 ^ pu];
+        tab[slot_of(uu, vv, f)] = make_int4(c0, c1, c2, c3);
+        tab[slot_of(uu, vv, fm)] = make_int4(-c0, -c1, -c2, -c3);
+      }
     }
   }
 
@@ -553,19 +565,33 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
       for (int il = 0; il < IL; ++il)
 #pragma unroll
         for (int g = 0; g < GB; ++g) acc[il][g] = 0u;
+      // The lookups of CH steps are issued before any of their sums, so a
+      // wave keeps CH * NT * IL table reads in flight.
 #pragma unroll
-      for (int st = 0; st < S::NV; ++st) {
+      for (int st0 = 0; st0 < S::NV; st0 += CH) {
+        int4 e[CH][IL][NT];
 #pragma unroll
-        for (int il = 0; il < IL; ++il) {
-          const uint32_t addr =
-              and_or(field_shl8_raw<S::WL>(w[il], st * S::FB, S::FB), fmask, boff[st]);
+        for (int sc = 0; sc < CH; ++sc) {
 #pragma unroll
-          for (int t4 = 0; t4 < NT; ++t4) {
-            const int4 e = *reinterpret_cast<const int4*>(lut_bytes + addr + t4 * S::TBYTES);
-            acc[il][4 * t4 + 0] += static_cast<uint32_t>(e.x);
-            acc[il][4 * t4 + 1] += static_cast<uint32_t>(e.y);
-            acc[il][4 * t4 + 2] += static_cast<uint32_t>(e.z);
-            acc[il][4 * t4 + 3] += static_cast<uint32_t>(e.w);
+          for (int il = 0; il < IL; ++il) {
+            const uint32_t addr = and_or(
+                field_shl8_raw<S::WL>(w[il], (st0 + sc) * S::FB, S::FB), fmask, boff[st0 + sc]);
+#pragma unroll
+            for (int t4 = 0; t4 < NT; ++t4)
+              e[sc][il][t4] = *reinterpret_cast<const int4*>(lut_bytes + addr + t4 * S::TBYTES);
+          }
+        }
+#pragma unroll
+        for (int sc = 0; sc < CH; ++sc) {
+#pragma unroll
+          for (int il = 0; il < IL; ++il) {
+#pragma unroll
+            for (int t4 = 0; t4 < NT; ++t4) {
+              acc[il][4 * t4 + 0] += static_cast<uint32_t>(e[sc][il][t4].x);
+              acc[il][4 * t4 + 1] += static_cast<uint32_t>(e[sc][il][t4].y);
+              acc[il][4 * t4 + 2] += static_cast<uint32_t>(e[sc][il][t4].z);
+              acc[il][4 * t4 + 3] += static_cast<uint32_t>(e[sc][il][t4].w);
+            }
           }
         }
       }
