@@ -10,6 +10,9 @@ in HBM before timing starts.
 Prints one JSON line.  Per-kernel durations come from HIP events recorded on
 the stream the kernels run on; the score kernel is also timed alone on a cold
 cache (2 GiB of reads between launches) for its HBM roofline.
+
+With --workloads it instead prints one JSON line per workload shape with the
+write and score kernel times (--steps launches each after --warmup).
 """
 
 import argparse
@@ -52,6 +55,40 @@ def counter_traffic(kernel):
     return entry["bytes"] if h.hexdigest() == entry["sha1"] else None
 
 
+WARM_MS = 30.0   # time each kernel runs untimed before its timed launches
+
+
+def launches_ms(torch, stream, fn, reps, warm_ms=WARM_MS):
+    """Average duration of `reps` back-to-back launches of fn, from HIP events
+    recorded on the stream the kernels run on.  Before the start event the
+    kernel runs untimed for `warm_ms` of wall time, and a few more launches
+    are queued right before the event: the chip needs several milliseconds of
+    a given load before its clock settles (the first couple of hundred score
+    launches after other work run up to a third slower), and that transient
+    belongs to neither kernel.  Python's cyclic garbage collector is held
+    off (a full collection of this process stalls the launching thread for
+    tens of milliseconds)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gc.collect()
+    gc.disable()
+    try:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warm_ms * 1e-3:
+            for _ in range(8):
+                fn()
+            torch.cuda.synchronize()
+        for _ in range(8):
+            fn()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
+    return e0.elapsed_time(e1) / reps
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -63,7 +100,61 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cold-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workloads", action="store_true",
+                    help="instead of the benchmark line: time the write and score kernels "
+                         "on every workload shape, one JSON line per workload")
     return ap.parse_args()
+
+
+def workload_table(args):
+    """Write and score kernel times on every workload shape: each kernel is
+    launched `steps` times back to back between HIP events on its stream,
+    right behind untimed launches of the same kernel (inputs resident in
+    HBM, Python's collector off)."""
+    import torch
+    import lut_attention_scoring_amd as axr
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def per_launch_ms(fn):
+        return launches_ms(torch, stream, fn, args.steps)
+
+    cases = [("tiny_d128_b3", lambda: W.tiny()),
+             ("llama31_8b_decode_d128_b3", lambda: W.llama_decode()),
+             ("qwen25_3b_layer0_d128_b4", lambda: W.qwen_layer(0)),
+             ("qwen25_3b_layer35_d128_b4", lambda: W.qwen_layer(W.QWEN_LAYERS - 1))]
+    cases += [(f"long_context_d128_b{b}", lambda b=b: W.long_context(b=b)) for b in (2, 3, 4)]
+    cases += [(f"write_sweep_d{d}_b{b}", lambda d=d, b=b: W.write_sweep(d=d, b=b))
+              for d in (128, 256, 512) for b in (2, 3, 4)]
+    for name, make in cases:
+        w = make()
+        keys = w["keys"].to(dev)
+        B, Hkv, T, d = keys.shape
+        b, bits = w["b"], w["sign_bits"]
+        n = B * Hkv * T
+        packed, norms = axr.quantize_keys(keys, bits, b)
+        write_ms = per_launch_ms(lambda: axr.quantize_keys(keys, bits, b, packed=packed,
+                                                           norms=norms))
+        write_bytes = n * (d * keys.element_size() + d * b // 8 + 4)
+        line = {"workload": name, "keys": n, "d": d, "b": b, "key_dtype": str(keys.dtype),
+                "write_us": write_ms * 1e3, "write_GB_per_s": write_bytes / (write_ms * 1e6),
+                "write_frac_hbm": write_bytes / (write_ms * 1e6) / HBM_PEAK_GBS}
+        if w["q"] is not None:
+            q = w["q"].to(dev)
+            Hq = q.shape[1]
+            scores = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
+            score_ms = per_launch_ms(lambda: axr.score(q, packed, norms, bits, b, out=scores))
+            score_bytes = n * (d * b // 8 + 4 + 4 * (Hq // Hkv))
+            line.update({"G": Hq // Hkv, "score_us": score_ms * 1e3,
+                         "score_GB_per_s": score_bytes / (score_ms * 1e6),
+                         "score_frac_hbm": score_bytes / (score_ms * 1e6) / HBM_PEAK_GBS})
+            del q, scores
+        print(json.dumps(line), flush=True)
+        del keys, packed, norms, w
+        torch.cuda.empty_cache()
 
 
 def cpu_baseline(w):
@@ -94,10 +185,13 @@ def cpu_baseline(w):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the score and write paths shard with no exchange; see DESIGN.md)",
+        print("bench.py measures one GPU: there is no multi-GPU path "
+              "(the score and write paths shard with no exchange)",
               file=sys.stderr)
         sys.exit(2)
+    if args.workloads:
+        workload_table(args)
+        return
 
     import torch
     import lut_attention_scoring_amd as axr
@@ -122,15 +216,14 @@ def main():
         axr.quantize_keys(keys, bits, b, packed=packed, norms=norms)
         axr.score(q, packed, norms, bits, b, out=scores)
 
-    log(f"warmup {args.warmup}")
+    # The collector runs before the warmup, so that the GPU idles only for
+    # the synchronisation between the warmup and the timed steps.
+    log(f"warmup {args.warmup}, timing {args.steps} steps")
+    gc.collect()
+    gc.disable()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    gc.collect()
-    gc.disable()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -140,24 +233,7 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
 
     def per_launch_ms(fn, reps):
-        """Average duration of `reps` back-to-back launches of fn, from HIP
-        events recorded on the stream the kernels run on.  Python's cyclic
-        garbage collector is held off inside the timed loop (a full
-        collection of this process stalls the launching thread for tens of
-        milliseconds)."""
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        gc.collect()
-        gc.disable()
-        try:
-            e0.record(stream)
-            for _ in range(reps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-        finally:
-            gc.enable()
-        return e0.elapsed_time(e1) / reps
+        return launches_ms(torch, stream, fn, reps)
 
     log("per-kernel timing")
     write_ms = per_launch_ms(lambda: axr.quantize_keys(keys, bits, b, packed=packed, norms=norms),
