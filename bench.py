@@ -37,11 +37,11 @@ CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
 # files below); otherwise traffic is reported as null.
 COUNTER_TRAFFIC = {
     "write": {"sources": ["axr_write.hip", "axr_keyquant.h", "axr_device.h", "axr_internal.h"],
-              "sha1": "b09a3fff888a695c0ebd6b23e9eea6617786dcf4",
-              "bytes": (262203.5 * 2.0 + 107146.5) * 1024},
+              "sha1": "233f3a113706934fa9346743f799908a11518c6e",
+              "bytes": (262190.1 * 2.0 + 106546.6) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
               "sha1": "435ee0628b394fe7c04c0688888feb235f74fd12",
-              "bytes": (53433.2 * 2.0 + 34827.3) * 1024},
+              "bytes": (53431.3 * 2.0 + 35156.9) * 1024},
 }
 
 
@@ -307,8 +307,8 @@ def main():
     cold_ms = cold[len(cold) // 2]
 
     # Achievable-bandwidth ceilings on this machine (include/axr_probe.h): a
-    # bare 2 GiB read stream, and a stream with the score kernel's traffic
-    # (its read bytes, then its write bytes, per block).
+    # bare 2 GiB read stream, and streams with the score kernel's and the
+    # write kernel's traffic (read bytes, then write bytes, per block).
     log("bandwidth probes")
     psink = torch.zeros(4, dtype=torch.int32, device=dev)
     read_ms = per_launch_ms(lambda: axr.probe_read_stream(flush, psink), 10)
@@ -316,7 +316,13 @@ def main():
     score_out = n * 4 * (Hq // Hkv)
     shaped_ms = per_launch_ms(lambda: axr.probe_read_write(keys, score_in, scores, score_out),
                               args.steps)
-    del flush, sink
+    # and one with the write kernel's traffic (the keys in, records and norms out)
+    write_in = n * d * keys.element_size()
+    write_out = n * (d * b // 8 + 4)
+    wscratch = torch.empty(write_out, dtype=torch.uint8, device=dev)
+    wshaped_ms = per_launch_ms(lambda: axr.probe_read_write(keys, write_in, wscratch, write_out),
+                               args.steps)
+    del flush, sink, wscratch
 
     # Write path with the comparison transforms (block-quaternion rotations)
     # on the prefill write-sweep keys, b = 3.
@@ -392,6 +398,9 @@ def main():
             "score_shaped_stream_GB_per_s": (score_in + score_out) / (shaped_ms * 1e-3) / 1e9,
             "score_shaped_stream_ms": shaped_ms,
             "score_frac_of_shaped_stream": shaped_ms / score_ms,
+            "write_shaped_stream_GB_per_s": (write_in + write_out) / (wshaped_ms * 1e-3) / 1e9,
+            "write_shaped_stream_ms": wshaped_ms,
+            "write_frac_of_shaped_stream": wshaped_ms / write_ms,
         },
         "kernels": {
             "write": {"ms": write_ms, "keys_per_s": n / (write_ms * 1e-3),

@@ -199,7 +199,13 @@ int launch_t(const void* keys, int64_t n, const WriteParams& p, uint32_t* packed
              float* y, int mode, hipStream_t s) {
   constexpr int KPB = kBlock / (D / 32);
   const int64_t need = (n + KPB - 1) / KPB;
-  const int grid = static_cast<int>(need < 4096 ? need : 4096);
+  // Two batches of keys per block: a measured optimum on every workload
+  // shape between one batch per block (block start-up dominates) and a
+  // capped grid of long-running blocks (uneven finish at the end).
+  int64_t blocks = (need + 1) / 2;
+  if (blocks > (int64_t{1} << 30)) blocks = int64_t{1} << 30;   // the loop covers the rest
+  const int grid = static_cast<int>(blocks);
+  if (grid == 0) return 0;
   hipLaunchKernelGGL((write_kernel<D, BITS, DT, TF>), dim3(grid), dim3(kBlock), 0, s, keys, n,
                      p, packed, norms, y, mode);
   return static_cast<int>(hipGetLastError());
