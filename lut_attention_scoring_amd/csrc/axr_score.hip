@@ -443,32 +443,32 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
       const int f0 = item / GROUPS;
       const int j = 32 * uu + P * vv;
       int4* tab = lut + t4 * (S::TBYTES / 16);
-      // q'_j 2^e (exact: the scale is a power of two) for the four heads
+      // With four lanes per key, component i of chunk u's entries holds head
+      // u ^ i (see quad_reduce_scatter); otherwise heads are in order.  The
+      // coordinates are read in that order, q'_j 2^e (exact: the scale is a
+      // power of two).
+      const int pu = S::LPK == 4 ? (uu & 3) : 0;
       float qa[4], qb[4];
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const int g = 4 * t4 + hh;
-        qa[hh] = qs[g][j] * hscale[g];
-        qb[hh] = P == 2 ? qs[g][j + P - 1] * hscale[g] : 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        const int g = 4 * t4 + (i ^ pu);
+        qa[i] = qs[g][j] * hscale[g];
+        qb[i] = P == 2 ? qs[g][j + P - 1] * hscale[g] : 0.0f;
       }
       for (int f = f0; f < HALF_NE; f += FSPLIT) {
         int e[4];
 #pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
+        for (int i = 0; i < 4; ++i) {
           if constexpr (P == 1) {
-            e[hh] = __float2int_rn(qa[hh] * cent[f]);
+            e[i] = __float2int_rn(qa[i] * cent[f]);
           } else {
-            e[hh] = __float2int_rn(qa[hh] * cent[f & (L - 1)]) +
-                    __float2int_rn(qb[hh] * cent[f >> BITS]);
+            e[i] = __float2int_rn(qa[i] * cent[f & (L - 1)]) +
+                   __float2int_rn(qb[i] * cent[f >> BITS]);
           }
         }
         const int fm = (S::NE - 1) ^ f;            // every field mirrored
-        // With four lanes per key, component i of chunk u's entries holds head
-        // u ^ i (see quad_reduce_scatter); otherwise heads are in order.
-        const int pu = S::LPK == 4 ? (uu & 3) : 0;
-        const int c0 = e[0 ^ pu], c1 = e[1 ^ pu], c2 = e[2 ^ pu], c3 = e[3 ^ pu];
-        tab[slot_of(uu, vv, f)] = make_int4(c0, c1, c2, c3);
-        tab[slot_of(uu, vv, fm)] = make_int4(-c0, -c1, -c2, -c3);
+        tab[slot_of(uu, vv, f)] = make_int4(e[0], e[1], e[2], e[3]);
+        tab[slot_of(uu, vv, fm)] = make_int4(-e[0], -e[1], -e[2], -e[3]);
       }
     }
   }
