@@ -129,6 +129,23 @@ def test_score_wide_heads(d, b):
     _score_and_check(q, keys, packed, norms, bits, b, f"wide score d={d} b={b}")
 
 
+@pytest.mark.parametrize("G,b", [(4, 3), (8, 2), (8, 4)])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 1023, 1024, 1025, 4097])
+def test_score_unit_and_tile_edges(T, G, b):
+    """Blocks hand out 16-token units from a counter: lengths one short of,
+    equal to and one past a unit and a 1024-token tile, a tile holding a
+    single token, and caches longer than the scored prefix."""
+    d, Bn, Hkv = 128, 1, 1
+    rng = np.random.default_rng(7000 + T + 10 * G + b)
+    t_cap = T + 5
+    keys = torch.from_numpy(rng.standard_normal((Bn, Hkv, t_cap, d)).astype(np.float32)
+                            ).to(torch.float16)
+    q = torch.from_numpy(rng.standard_normal((Bn, Hkv * G, d)).astype(np.float32)).to(torch.float16)
+    bits = W.sign_bits(d)
+    packed, norms = _write_and_check(keys, bits, b, f"edges T={T}")
+    _score_and_check(q, keys, packed, norms, bits, b, f"edges score T={T} G={G} b={b}", T=T)
+
+
 # ---------------------------------------------------------------------------
 # Edge cases.
 # ---------------------------------------------------------------------------
