@@ -97,7 +97,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    # ~17 ms of steps: the clock takes ~10 ms of this load to settle
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cold-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workloads", action="store_true",
