@@ -188,6 +188,9 @@ static int check_score_sizes(int d, int b, int q_dtype, const uint32_t* sign_bit
   if (T > 0 && T * static_cast<int64_t>(d) * b / 8 > INT32_MAX)
     return fail(AXR_EUNSUPPORTED, "T=%lld tokens exceed 2 GiB of records per row",
                 static_cast<long long>(T));
+  // (this also bounds the score rows of one block's query heads, addressed
+  // the same way: at most 8 heads x 4 B per token, never more than the
+  // d*b/8 >= 32 B of a record)
   return AXR_OK;
 }
 

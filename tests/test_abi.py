@@ -142,6 +142,9 @@ def test_score_rejects_rows_beyond_32bit_offsets():
     # 2^31 bytes of d=128, b=3 records is 44.7M tokens per row
     st, msg = _s(T=45_000_000, t_cap=45_000_000)
     assert st == axr.EUNSUPPORTED and "2 GiB" in msg
+    # the smallest record (d=128, b=2: 32 B) bounds eight heads' score rows
+    st, msg = _s(T=67_108_864, t_cap=67_108_864, b=2, Hq=16, Hkv=2)
+    assert st == axr.EUNSUPPORTED and "2 GiB" in msg
 
 
 def _a(keys=FAKE, dtype=axr.F16, B=2, Hkv=4, d=128, b=3, signs=SIGNS, pos=FAKE, t_cap=64,
