@@ -38,10 +38,10 @@ CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
 COUNTER_TRAFFIC = {
     "write": {"sources": ["axr_write.hip", "axr_keyquant.h", "axr_device.h", "axr_internal.h"],
               "sha1": "233f3a113706934fa9346743f799908a11518c6e",
-              "bytes": (262190.1 * 2.0 + 106546.6) * 1024},
+              "bytes": (262190.1 * 2.0 + 106547.3) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "435ee0628b394fe7c04c0688888feb235f74fd12",
-              "bytes": (53431.3 * 2.0 + 35156.9) * 1024},
+              "sha1": "18a3f8d341aa6517f5f437026498b71031b45a1f",
+              "bytes": (53430.8 * 2.0 + 35088.9) * 1024},
 }
 
 
