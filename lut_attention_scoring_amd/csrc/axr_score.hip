@@ -18,9 +18,14 @@
 //     fp32 multiply.
 //   * loop: a key is read by LPK = d/32 adjacent lanes, lane u owning the
 //     32 coordinates [32u, 32u+32) = b words of the record, so a wave reads
-//     a contiguous span of records.  Each lane looks up its groups, the
-//     lanes of a key sum their partial results across lanes, and each lane
-//     writes the scores of its heads.
+//     a contiguous span of records.  Each lane looks up its groups (several
+//     lookups issued before any of their sums), the lanes of a key sum their
+//     partial results across lanes, and each lane writes the scores of its
+//     heads.
+//   * work split: one block per CU; the block's tile is cut into units of
+//     one wave's keys, handed out by a per-block LDS counter, so the waves
+//     that the SIMD's issue arbitration favours take more units and all
+//     waves of the block finish together.
 //   * LDS banks: 16-byte reads are conflict-free when the 16 lanes of a
 //     quarter-wave touch 16 different 16-byte columns of a 256-byte row.  The
 //     table puts group v of lane-chunk u in column (v + KPG*u) mod 16 and each
@@ -141,20 +146,9 @@ struct ScoreShape {
 constexpr int IL = 1;                // record units processed together
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit dword format
 
-// (field << 8) for the width-bit field at bit pos of an N-word bit string,
-// ready to be or-ed into a table address (bits 8 .. 8 + width).
-template <int N>
-__device__ __forceinline__ uint32_t field_shl8(const uint32_t (&w)[N], int pos, int width) {
-  const int wi = pos >> 5, sh = pos & 31;
-  const uint32_t mask = ((1u << width) - 1u) << 8;
-  if (sh + width <= 32) {
-    if (sh >= 8) return (w[wi] >> (sh - 8)) & mask;
-    return (w[wi] << (8 - sh)) & mask;
-  }
-  return __builtin_amdgcn_alignbit(w[(wi + 1) % N], w[wi], sh - 8) & mask;
-}
-
-// The same bits before masking (the caller masks with ((1 << width) - 1) << 8).
+// The width-bit field at bit pos of an N-word bit string, moved to bits
+// 8 .. 8 + width (other bits are left; the caller masks with
+// ((1 << width) - 1) << 8 and ors the result into a table address).
 template <int N>
 __device__ __forceinline__ uint32_t field_shl8_raw(const uint32_t (&w)[N], int pos, int width) {
   const int wi = pos >> 5, sh = pos & 31;
