@@ -40,7 +40,7 @@ COUNTER_TRAFFIC = {
               "sha1": "233f3a113706934fa9346743f799908a11518c6e",
               "bytes": (262190.1 * 2.0 + 106547.3) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "18a3f8d341aa6517f5f437026498b71031b45a1f",
+              "sha1": "60c6d3ff25851bf3c0f482891851c54370dbafd8",
               "bytes": (53430.8 * 2.0 + 35088.9) * 1024},
 }
 
