@@ -204,7 +204,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   // NT tables of S::TBYTES bytes, q' [GB][D] and the head scales.
   __shared__ int4 lut[NT * (S::TBYTES / 16)];
   __shared__ float qs[GB][D];
-  __shared__ float hscale[GB], hinv[GB];
+  __shared__ float hscale[GB], hinv[GB];       // 2^e and 2^-e of each head's
+  __shared__ float hscale2[GB], hinv2[GB];     // scale, as two exact factors
   __shared__ float cent[16];
 
   const int tid = threadIdx.x;
@@ -341,9 +342,14 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
       int e = 0;
       if (f > 0.0f) frexpf(f, &e);              // f < 2^e
       int sh = 30 - e;
-      sh = sh > 126 ? 126 : (sh < -126 ? -126 : sh);
-      hscale[g] = ldexpf(1.0f, sh);
-      hinv[g] = ldexpf(1.0f, -sh);
+      // up to 2^252 for tiny queries, applied as two powers of two that are
+      // each representable (the second is 1 unless sh > 126)
+      sh = sh > 252 ? 252 : (sh < -126 ? -126 : sh);
+      const int sh1 = sh > 126 ? 126 : sh;
+      hscale[g] = ldexpf(1.0f, sh1);
+      hinv[g] = ldexpf(1.0f, -sh1);
+      hscale2[g] = ldexpf(1.0f, sh - sh1);
+      hinv2[g] = ldexpf(1.0f, sh1 - sh);
     }
   }
   // Fused decode step: one wave quantizes the new key with the write path's
@@ -446,8 +452,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int g = 4 * t4 + (i ^ pu);
-        qa[i] = qs[g][j] * hscale[g];
-        qb[i] = P == 2 ? qs[g][j + P - 1] * hscale[g] : 0.0f;
+        qa[i] = (qs[g][j] * hscale[g]) * hscale2[g];
+        qb[i] = P == 2 ? (qs[g][j + P - 1] * hscale[g]) * hscale2[g] : 0.0f;
       }
       for (int f = f0; f < HALF_NE; f += FSPLIT) {
         int e[4];
@@ -486,18 +492,24 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
       static_cast<int>(static_cast<uint32_t>(nvalid) * static_cast<uint32_t>(prm.T) * 4u),
       kRsrcWord3);
   uint32_t vsc[NT];
-  float ginv_u[NT];
+  float ginv_u[NT], ginv2_u[NT];
 #pragma unroll
   for (int t4 = 0; t4 < NT; ++t4) {
     const uint32_t g = static_cast<uint32_t>((4 * t4 + u) % GB);
     vsc[t4] = (g * static_cast<uint32_t>(prm.T) + static_cast<uint32_t>(t0 + kw)) * 4u;
   }
   __syncthreads();
-  float ginv[GB];                               // 2^-e per head
+  float ginv[GB], ginv2[GB];                    // 2^-e per head, two factors
 #pragma unroll
-  for (int g = 0; g < GB; ++g) ginv[g] = hinv[g];
+  for (int g = 0; g < GB; ++g) {
+    ginv[g] = hinv[g];
+    ginv2[g] = hinv2[g];
+  }
 #pragma unroll
-  for (int t4 = 0; t4 < NT; ++t4) ginv_u[t4] = hinv[(4 * t4 + u) % GB];
+  for (int t4 = 0; t4 < NT; ++t4) {
+    ginv_u[t4] = hinv[(4 * t4 + u) % GB];
+    ginv2_u[t4] = hinv2[(4 * t4 + u) % GB];
+  }
 
   // 3. stream the tile, keeping PD units of records in flight and working
   //    on IL of them at once (independent lookups interleave in the LDS
@@ -602,7 +614,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
                                     acc[il][4 * t4 + 3]};
             const uint32_t tot = quad_reduce_scatter(a4);
             const float sv =
-                nk[il] * (static_cast<float>(static_cast<int32_t>(tot)) * ginv_u[t4]);
+                (nk[il] * (static_cast<float>(static_cast<int32_t>(tot)) * ginv_u[t4])) *
+                ginv2_u[t4];
             if (valid && 4 * t4 + u < nvalid) {
               __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), rsc,
                                                     vsc[t4], tb_rel * 4u, 0);
@@ -623,8 +636,9 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
             for (int g = 0; g < GB; ++g) {
               if (g % S::LPK == u && g < nvalid) {
                 const float sc = static_cast<float>(static_cast<int32_t>(acc[il][g])) * ginv[g];
-                scores[(static_cast<size_t>(bi) * prm.Hq + h0 + g) * prm.T + t] = nk[il] * sc;
-                if (want_lse) lse_push(sm_m[0], sm_l[0], nk[il] * sc * lse_scale);
+                const float sv = (nk[il] * sc) * ginv2[g];
+                scores[(static_cast<size_t>(bi) * prm.Hq + h0 + g) * prm.T + t] = sv;
+                if (want_lse) lse_push(sm_m[0], sm_l[0], sv * lse_scale);
               }
             }
           }

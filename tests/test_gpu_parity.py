@@ -215,6 +215,35 @@ def test_extreme_magnitudes_fp32():
     _score_and_check(q, keys, packed, norms, bits, 3, "extreme magnitudes score")
 
 
+@pytest.mark.parametrize("G", [4, 8])
+def test_query_magnitude_edges(G):
+    """The table's fixed-point scale is chosen per head from the query: a
+    zero query scores exactly 0, and tiny (1e-36), single-coordinate and huge
+    (1e30) fp32 queries keep the score bound (scales beyond 2^126 are applied
+    as two exact factors)."""
+    d, b, T = 128, 3, 1500
+    rng = np.random.default_rng(4242 + G)
+    keys = torch.from_numpy(rng.standard_normal((1, 1, T, d)).astype(np.float32)).to(torch.float16)
+    q = rng.standard_normal((1, G, d))
+    q[0, 0] = 0.0
+    q[0, 1] *= 1e-36
+    q[0, 2] = 0.0
+    q[0, 2, 7] = 1e-30
+    q[0, 3] *= 1e30
+    if G == 8:
+        q[0, 4] *= 1e-20
+        q[0, 5] *= 1e20
+        q[0, 6] = 0.0
+        q[0, 6, 100] = -3.0
+    qt = torch.from_numpy(q.astype(np.float32))
+    bits = W.sign_bits(d)
+    packed, norms = _write_and_check(keys, bits, b, f"q edges G={G}")
+    _score_and_check(qt, keys, packed, norms, bits, b, f"q edges score G={G}")
+    scores = axr().score(qt.to(DEV), packed, norms, bits, b)
+    torch.cuda.synchronize()
+    assert torch.all(scores[0, 0] == 0), "a zero query must score exactly 0"
+
+
 def test_score_is_deterministic_and_tile_independent():
     m = axr()
     w = W.llama_decode(B=1, Hkv=2, Hq=8, T=5000)
