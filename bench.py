@@ -37,11 +37,11 @@ CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
 # files below); otherwise traffic is reported as null.
 COUNTER_TRAFFIC = {
     "write": {"sources": ["axr_write.hip", "axr_keyquant.h", "axr_device.h", "axr_internal.h"],
-              "sha1": "233f3a113706934fa9346743f799908a11518c6e",
-              "bytes": (262190.1 * 2.0 + 106547.3) * 1024},
+              "sha1": "cf78847eb64e8f04264a3217b181487a7d5f8869",
+              "bytes": (262200.6 * 2.0 + 106547.9) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "60c6d3ff25851bf3c0f482891851c54370dbafd8",
-              "bytes": (53430.8 * 2.0 + 35088.9) * 1024},
+              "sha1": "0bc7176f186e6e19bcbc608f4c045a8a473b465f",
+              "bytes": (53432.2 * 2.0 + 34534.7) * 1024},
 }
 
 
