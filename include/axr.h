@@ -75,9 +75,9 @@ int axr_codebook(int d, int b, double* centroids, double* thresholds);
  * Write path (AXELRAM, Abstract: transform on write, quantize once).
  * For each of the n keys k (rows of `keys`):
  *   ||k|| is stored in norms[i] (fp32, accumulated in fp32; a key whose
- *   squared entries underflow fp32 takes it from its transformed
- *   coordinates scaled by 2^64, so tiny keys keep full precision until
- *   their entries are fp32 denormals);
+ *   squared entries underflow or overflow fp32 takes it from its
+ *   transformed coordinates scaled by 2^64 or 2^-64, so keys keep full
+ *   precision from fp32 denormal entries up to ~1e36);
  *   y = H_d (s * k) / (sqrt(d) ||k||)       (y = 0 for a zero key);
  *   idx_j = number of codebook thresholds strictly below y_j, in [0, 2^b);
  *   the indices are packed into packed[i*W .. i*W + W) as described above.

@@ -142,20 +142,24 @@ __device__ __forceinline__ float key_norm(float ss) {
 }
 
 // A key whose squares underflow fp32 (every |k_j| below ~1e-19) comes out of
-// key_norm far below 2^-50.  Its norm is then taken again from its
-// transformed coordinates x, scaled by 2^64 (exact): the transform keeps the
+// key_norm far below 2^-50, and one whose squares overflow (|k_j| above
+// ~1.8e19) as inf.  Such a norm is taken again from the key's transformed
+// coordinates x scaled by 2^64 or 2^-64 (exact): the transform keeps the
 // norm up to the factor 1 / inv_sqrt_d.  All lanes of a key take the same
 // branch, so the lane exchanges stay among active lanes.
 template <int LPK>
-__device__ __forceinline__ float tiny_key_norm(float nrm, const float (&x)[32], float inv_sqrt_d) {
-  if (nrm >= 0x1p-50f) return nrm;
+__device__ __forceinline__ float rescued_key_norm(float nrm, const float (&x)[32],
+                                                  float inv_sqrt_d) {
+  if (nrm >= 0x1p-50f && nrm <= 0x1p50f) return nrm;
+  const bool tiny = !(nrm >= 0x1p-50f);         // also NaN, which stays NaN
+  const float up = tiny ? 0x1p64f : 0x1p-64f;
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const float t = x[i] * 0x1p64f;
+    const float t = x[i] * up;
     ss = fmaf(t, t, ss);
   }
-  return (key_norm<LPK>(ss) * 0x1p-64f) * inv_sqrt_d;
+  return (key_norm<LPK>(ss) * (tiny ? 0x1p-64f : 0x1p64f)) * inv_sqrt_d;
 }
 
 // The sign pattern and the Walsh-Hadamard transform for lane u of a key.

@@ -377,14 +377,16 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
     ss += lane_xor<32>(ss);
     float nrm = sqrtf(ss);
     wht_row<R>(kv, lane);
-    if (!(nrm >= 0x1p-50f)) {
-      // squares that underflow fp32: the norm again from the transformed
-      // coordinates scaled by 2^64 (exact; the transform scales norms by
-      // sqrt(d)), as the write path does
+    if (!(nrm >= 0x1p-50f && nrm <= 0x1p50f)) {
+      // squares that underflow or overflow fp32: the norm again from the
+      // transformed coordinates scaled by 2^64 or 2^-64 (exact; the
+      // transform scales norms by sqrt(d)), as the write path does
+      const bool tiny = !(nrm >= 0x1p-50f);
+      const float up = tiny ? 0x1p64f : 0x1p-64f;
       float s2 = 0.0f;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float t = kv[r] * 0x1p64f;
+        const float t = kv[r] * up;
         s2 = fmaf(t, t, s2);
       }
       s2 += lane_xor<1>(s2);
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
       s2 += lane_xor<8>(s2);
       s2 += lane_xor<16>(s2);
       s2 += lane_xor<32>(s2);
-      nrm = (sqrtf(s2) * 0x1p-64f) * (1.0f / sqrtf(static_cast<float>(D)));
+      nrm = (sqrtf(s2) * (tiny ? 0x1p-64f : 0x1p64f)) * (1.0f / sqrtf(static_cast<float>(D)));
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kBlock) void write_kernel(const void* __restrict__ 
       for (int k = 0; k < 8; ++k) quat_block<TF == kIsoFull>(&x[4 * k], qa[k], qb[k]);
     }
 
-    nrm = tiny_key_norm<LPK>(nrm, x, prm.inv_sqrt_d);
+    nrm = rescued_key_norm<LPK>(nrm, x, prm.inv_sqrt_d);
 
     if (mode == kWriteQuantize) {
       float S[8];

@@ -289,10 +289,12 @@ def test_fused_decode_step(d, b, G, dtype):
                       f"{label} bi={bi}")
 
 
+@pytest.mark.parametrize("scale", [3e-30, 3e25])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_decode_tiny_new_keys(dtype):
-    """New keys whose squared entries underflow fp32, appended by the write
-    kernel and by the fused decode step: records and norms as the oracle's."""
+def test_decode_tiny_and_huge_new_keys(dtype, scale):
+    """New keys whose squared entries underflow or overflow fp32, appended by
+    the write kernel and by the fused decode step: records and norms as the
+    oracle's."""
     m = axr()
     rng = np.random.default_rng(5151)
     d, b, Hkv, G, t_cap, T = 128, 3, 2, 4, 600, 600
@@ -300,7 +302,7 @@ def test_decode_tiny_new_keys(dtype):
     B = len(pos)
     bits = W.sign_bits(d)
     cache = _keys(rng, (B, Hkv, t_cap, d), dtype)
-    new = _keys(rng, (B, Hkv, d), dtype, scale=3e-30)
+    new = _keys(rng, (B, Hkv, d), dtype, scale=scale)
     q = _keys(rng, (B, Hkv * G, d), dtype, scale=1.0)
     pos_t = torch.tensor(pos, dtype=torch.int32, device=DEV)
     for fused in (False, True):
@@ -311,7 +313,7 @@ def test_decode_tiny_new_keys(dtype):
             m.append_keys(new.to(DEV), bits, b, packed, norms, pos_t)
         torch.cuda.synchronize()
         assert _check_appended(new, packed, norms, pos, bits, b,
-                               f"tiny new keys fused={fused}") == B
+                               f"new keys at {scale:g} fused={fused}") == B
 
 
 def test_fused_decode_step_matches_two_launches():

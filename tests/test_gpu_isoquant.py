@@ -68,6 +68,20 @@ def test_isoquant_write_ragged(d, b, dtype, full):
 
 
 @pytest.mark.parametrize("full", [True, False])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_isoquant_tiny_and_huge_keys(dtype, full):
+    """Keys whose squares underflow or overflow fp32 take their norm from the
+    rotated coordinates, as in the Hadamard path."""
+    rng = np.random.default_rng(3300)
+    d, b, n = 128, 3, 256
+    k = rng.standard_normal((1, 1, n, d))
+    k[0, 0, 0::3] *= 1e-30
+    k[0, 0, 1::3] *= 1e28
+    keys = torch.from_numpy(k.astype(np.float32)).to(dtype)
+    _check(keys, b, full, f"isoquant tiny/huge {dtype} full={full}")
+
+
+@pytest.mark.parametrize("full", [True, False])
 def test_isoquant_write_sweep_full_size_sampled(full):
     w = W.write_sweep(d=256, b=3)
     flat_n = w["keys"].numel() // 256

@@ -246,20 +246,20 @@ def test_query_magnitude_edges(G):
 
 @pytest.mark.parametrize("d", [128, 512])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("scale", [1e-25, 1e-33])
-def test_tiny_keys(scale, dtype, d):
-    """Keys whose squared entries underflow fp32, mixed token by token with
-    ordinary keys (both paths in one wave): the norm comes from the
-    transformed coordinates, so indices, norms and scores meet the same
+@pytest.mark.parametrize("scale", [1e-25, 1e-33, 1e25, 1e30])
+def test_tiny_and_huge_keys(scale, dtype, d):
+    """Keys whose squared entries underflow or overflow fp32, mixed token by
+    token with ordinary keys (both paths in one wave): the norm comes from
+    the transformed coordinates, so indices, norms and scores meet the same
     bounds as for any key."""
     b, Hkv, G, T = 3, 2, 4, 700
-    rng = np.random.default_rng(int(-np.log10(scale)) + d)
+    rng = np.random.default_rng(int(abs(np.log10(scale))) + d + (scale > 1))
     k = rng.standard_normal((1, Hkv, T, d))
     k[:, :, ::2] *= scale
     keys = torch.from_numpy(k.astype(np.float32)).to(dtype)
     q = torch.from_numpy(rng.standard_normal((1, Hkv * G, d)).astype(np.float32))
     bits = W.sign_bits(d)
-    label = f"tiny keys {scale:g} {dtype} d={d}"
+    label = f"keys at {scale:g} {dtype} d={d}"
     packed, norms = _write_and_check(keys, bits, b, label)
     _score_and_check(q, keys, packed, norms, bits, b, label)
 
