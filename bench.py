@@ -37,11 +37,11 @@ CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
 # files below); otherwise traffic is reported as null.
 COUNTER_TRAFFIC = {
     "write": {"sources": ["axr_write.hip", "axr_keyquant.h", "axr_device.h", "axr_internal.h"],
-              "sha1": "cf78847eb64e8f04264a3217b181487a7d5f8869",
-              "bytes": (262200.6 * 2.0 + 106547.9) * 1024},
+              "sha1": "d8f3e89891bc305824c1dfb73fb223c1cdfab921",
+              "bytes": (262195.6 * 2.0 + 106504.8) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "0bc7176f186e6e19bcbc608f4c045a8a473b465f",
-              "bytes": (53432.2 * 2.0 + 34534.7) * 1024},
+              "sha1": "24cbbc39a4a06d68c5e99fd9967b8767fe76716f",
+              "bytes": (53432.2 * 2.0 + 34495.7) * 1024},
 }
 
 
