@@ -37,8 +37,8 @@ CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
 # files below); otherwise traffic is reported as null.
 COUNTER_TRAFFIC = {
     "write": {"sources": ["axr_write.hip", "axr_keyquant.h", "axr_device.h", "axr_internal.h"],
-              "sha1": "d8f3e89891bc305824c1dfb73fb223c1cdfab921",
-              "bytes": (262195.6 * 2.0 + 106504.8) * 1024},
+              "sha1": "314c1d3c5fa3372c96f18d09fac7f006e90337f4",
+              "bytes": (262195.6 * 2.0 + 106534.7) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
               "sha1": "24cbbc39a4a06d68c5e99fd9967b8767fe76716f",
               "bytes": (53432.2 * 2.0 + 34495.7) * 1024},

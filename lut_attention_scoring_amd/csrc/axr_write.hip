@@ -65,10 +65,21 @@ __device__ __forceinline__ void quat_block(float* v, const float (&a)[4], const 
 }
 
 
+// Waves per SIMD the compiler is asked to fit: 6 (at most 80 VGPRs) for the
+// fp16 d = 128 Hadamard kernels with 2 or 3 bits, which would otherwise take
+// 81-82 VGPRs and run 5 waves per SIMD; the other instances already fit 6
+// waves or would spill under the cap, and keep the compiler's choice (1 sets
+// no bound).
+template <int D, int BITS, int DT, int TF>
+constexpr int write_waves() {
+  return (D == 128 && BITS <= 3 && DT == AXR_F16 && TF == kWht) ? 6 : 1;
+}
+
 // TF selects the transform: kWht (sign pattern + Walsh-Hadamard), or the
 // block-quaternion comparison transforms kIsoFull / kIsoFast.
 template <int D, int BITS, int DT, int TF>
-__global__ __launch_bounds__(kBlock) void write_kernel(const void* __restrict__ keys, int64_t n,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(write_waves<D, BITS, DT, TF>())))
+void write_kernel(const void* __restrict__ keys, int64_t n,
                                                      WriteParams prm,
                                                      uint32_t* __restrict__ packed,
                                                      float* __restrict__ norms,
