@@ -254,3 +254,43 @@ def test_decode_step_validation():
     assert ds(k=FAKE + 2)[0] == axr.EALIGN
     assert ds(packed=FAKE + 8)[0] == axr.EALIGN
     assert ds(B=0, q=None, k=None, pos=None, packed=None, norms=None, scores=None)[0] == axr.OK
+
+
+def test_codebook_cache_and_errors_are_thread_safe():
+    """Concurrent first solves of the same (d, b) keys agree with a serial
+    solve, and each thread reads back its own last-error message."""
+    import threading
+
+    keys = [(d, b) for d in range(3, 60, 4) for b in (1, 2, 3, 4)]
+    results = {}
+    errors = []
+    barrier = threading.Barrier(8)
+
+    def worker(tid):
+        barrier.wait()
+        mine = {}
+        order = keys[tid:] + keys[:tid]
+        for d, b in order:
+            mine[(d, b)] = axr.codebook(d, b)
+            bad = -(1000 + 8 * d + tid)
+            st = axr.lib.axr_codebook(bad, b, None, None)
+            msg = axr.lib.axr_last_error().decode()
+            if st != axr.EINVAL or f"d={bad}" not in msg:
+                errors.append((tid, st, msg))
+        results[tid] = mine
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
+    for (d, b) in keys:
+        ref_c, ref_t = axr.codebook(d, b)
+        for tid in range(8):
+            c, t = results[tid][(d, b)]
+            np.testing.assert_array_equal(c, ref_c)
+            np.testing.assert_array_equal(t, ref_t)
+    oc, ot = A.lloyd_max_codebook(7, 3)
+    c, t = axr.codebook(7, 3)
+    assert np.max(np.abs(c - oc)) <= 1e-12 / math.sqrt(7)
