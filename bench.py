@@ -37,11 +37,11 @@ CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
 # files below); otherwise traffic is reported as null.
 COUNTER_TRAFFIC = {
     "write": {"sources": ["axr_write.hip", "axr_keyquant.h", "axr_device.h", "axr_internal.h"],
-              "sha1": "314c1d3c5fa3372c96f18d09fac7f006e90337f4",
-              "bytes": (262195.6 * 2.0 + 106534.7) * 1024},
+              "sha1": "9bc723f8f220a1ecb9a42111564482501f05fa5a",
+              "bytes": (262196.1 * 2.0 + 106531.1) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "24cbbc39a4a06d68c5e99fd9967b8767fe76716f",
-              "bytes": (53432.2 * 2.0 + 34495.7) * 1024},
+              "sha1": "9d40cc3e216f11a072404deb3886f0ec983099bd",
+              "bytes": (53432.2 * 2.0 + 34485.5) * 1024},
 }
 
 

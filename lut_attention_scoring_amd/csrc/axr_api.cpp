@@ -4,6 +4,7 @@
 
 #include "axr.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -76,6 +77,43 @@ int axr_codebook(int d, int b, double* centroids, double* thresholds) {
   return ok();
 }
 
+// Scale K of the 4-bit quantizer's cell table, in cells per unit of
+// z / ||k||.  The kernel compares z with the signed thresholds P_i ||k||
+// (P_i = -tpos, 0, +tpos), and |z| <= zmax ||k|| (sqrt(d) for the
+// unnormalised Hadamard transform, 1 for the rotations).  K is the smallest
+// value, stepping up from one cell per smallest threshold gap (so that no
+// cell holds two thresholds), that puts every nonzero P_i K + kCellMid at
+// least 0.05 of a cell from a cell boundary, within the table's reach
+// (zmax K <= kCellMid - 2).  The kernel's cell position is within ~1e-5 of a
+// cell of its exact value, so a z near a cell boundary is never near a
+// threshold other than 0, which lies exactly on boundary kCellMid, where
+// rounding cannot carry z across.
+static float cell_scale(const float* tpos, int half, double zmax) {
+  const int nt = 2 * half - 1;
+  double P[axr::kMaxLevels - 1];
+  for (int j = 0; j + 1 < half; ++j) {
+    P[half + j] = tpos[j];
+    P[half - 2 - j] = -static_cast<double>(tpos[j]);
+  }
+  P[half - 1] = 0.0;
+  double gap = P[1] - P[0];
+  for (int i = 1; i + 1 < nt; ++i) gap = std::min(gap, P[i + 1] - P[i]);
+  const double mid = axr::kCellMid;
+  const double Kmax = (mid - 2.0) / (zmax * 1.001);
+  for (double K = 1.001 / gap; K <= Kmax; K += 1e-4 / gap) {
+    const double Kf = static_cast<float>(K);   // the kernel's value
+    bool good = true;
+    for (int i = 0; i < nt && good; ++i) {
+      if (i == half - 1) continue;
+      const double t = P[i] * Kf + mid;
+      const double f = t - std::floor(t);
+      good = f >= 0.05 && f <= 0.95;
+    }
+    if (good) return static_cast<float>(K);
+  }
+  return 0.0f;   // no scale found: the kernel keeps its threshold search
+}
+
 // Write-kernel parameters: sign words and the positive thresholds scaled by
 // sqrt(d) (the kernel compares against them times the key's norm).
 // (The block-quaternion transform is orthonormal as it stands, so there the
@@ -90,6 +128,7 @@ static axr::WriteParams write_params(const uint32_t* sign_bits, int d, int b,
   const double sqrt_d = tf == axr::kWht ? std::sqrt(static_cast<double>(d)) : 1.0;
   for (int i = 0; i + 1 < half; ++i) p.tpos[i] = static_cast<float>(cb.threshold[half + i] * sqrt_d);
   p.inv_sqrt_d = static_cast<float>(1.0 / sqrt_d);
+  p.cell_k = b == 4 ? cell_scale(p.tpos, half, tf == axr::kWht ? sqrt_d : 1.0) : 0.0f;
   p.t_cap = 0;
   p.Hkv = 1;
   return p;

@@ -10,6 +10,8 @@ namespace axr {
 constexpr int kMaxD = 512;
 constexpr int kMaxSignWords = kMaxD / 32;
 constexpr int kMaxLevels = 16;  // 2^b for b <= 4
+constexpr int kCells = 192;          // cells of the 4-bit quantizer's table
+constexpr float kCellMid = 96.0f;    // the cell boundary of the middle threshold
 
 // Lloyd-Max quantizer for N(0, 1/d) in double precision, ascending.
 struct Codebook {
@@ -37,6 +39,9 @@ struct WriteParams {
   // Comparison transform (kIsoFull / kIsoFast): device float [d/4][2][4],
   // (left, right) unit quaternion of each block of 4 coordinates.
   const float* quats;
+  // Cells per unit of z / ||k|| of the 4-bit quantizer's cell table (see
+  // the write kernel); 0 for other bit widths.
+  float cell_k;
 };
 
 // Write-path transforms: the method's sign pattern + Walsh-Hadamard, and the

@@ -263,4 +263,28 @@ __device__ __forceinline__ void quantize_lane(const float (&x)[32], const float 
   }
 }
 
+// The 4-bit index of each of a lane's 32 coordinates from the cell table:
+// u = z kc + kCellMid (kc = K / ||k||, K the table's scale) falls in cell c,
+// which holds cnt thresholds below it and at most one more, nxt, inside it;
+// the index is cnt + (z > nxt ||k||), the number of thresholds strictly
+// below z.  Indices fill the record words a nibble at a time, highest
+// coordinate first.
+__device__ __forceinline__ void quantize_cells(const float (&x)[32], float kc, float nrm,
+                                               const uint2* cells, uint32_t (&words)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) words[i] = 0u;
+#pragma unroll
+  for (int r = 31; r >= 0; --r) {
+    const float z = x[r];
+    const float u = fmaf(z, kc, kCellMid);
+    uint32_t c;
+    asm("v_cvt_u32_f32 %0, %1" : "=v"(c) : "v"(u));   // saturating: < 0 -> 0
+    c = c < kCells - 1 ? c : kCells - 1;
+    const uint2 e = cells[c];
+    const float t = __uint_as_float(e.y) * nrm;
+    const uint32_t idx = e.x + (z > t ? 1u : 0u);
+    words[r >> 3] = (words[r >> 3] << 4) | idx;
+  }
+}
+
 }  // namespace axr

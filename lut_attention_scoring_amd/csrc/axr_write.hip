@@ -19,13 +19,18 @@
 // un-negated after the last stage.
 //
 // Quantization compares z = H(s*k) (before the 1/(sqrt(d)||k||) scale)
-// against thresholds multiplied by sqrt(d)||k||, by binary search on |z|
-// over the positive thresholds of the symmetric codebook, then mirrors for
-// z <= 0 (a coordinate equal to +0, and every coordinate of a zero key, takes
-// the cell just below the middle threshold 0, as a value equal to a
-// threshold does).  The b index bits of each coordinate are lane masks of
-// compares; they are appended to the record words most significant bit
-// first, one add-with-carry per bit.
+// against thresholds multiplied by sqrt(d)||k||.  For b = 2 and 3: binary
+// search on |z| over the positive thresholds of the symmetric codebook, then
+// the mirror image for z <= 0 (a coordinate equal to +0, and every
+// coordinate of a zero key, takes the cell just below the middle threshold
+// 0); the b index bits of each coordinate are lane masks of compares,
+// appended to the record words most significant bit first, one
+// add-with-carry per bit.  For b = 4 (fifteen thresholds, where that search
+// costs four compares, three selects and four carries per coordinate): a
+// table in LDS over uniform cells of z / ||k||, each holding at most one
+// threshold, gives the number of thresholds below the coordinate's cell and
+// the one inside it, so one compare finishes the index, which is packed a
+// nibble at a time.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -95,6 +100,30 @@ void write_kernel(const void* __restrict__ keys, int64_t n,
   float P[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) P[i] = prm.tpos[i];
+  // 4-bit quantizer's cell table: cell c (position u in [c, c + 1), with
+  // u = z cell_k / ||k|| + kCellMid) gets the number of signed thresholds
+  // -tpos[6], ..., -tpos[0], 0, tpos[0], ..., tpos[6] below c and the first
+  // one at or above c (+inf past the last).
+  __shared__ uint2 cells[BITS == 4 ? kCells : 1];
+  if constexpr (BITS == 4) {
+    for (int c = threadIdx.x; c < kCells; c += kBlock) {
+      uint32_t cnt = 0u;
+      float nxt = INFINITY;
+      bool found = false;
+#pragma unroll
+      for (int i = 0; i < 15; ++i) {
+        const float th = i < 7 ? -P[6 - i] : (i == 7 ? 0.0f : P[i - 8]);
+        if (fmaf(th, prm.cell_k, kCellMid) < static_cast<float>(c)) {
+          ++cnt;
+        } else if (!found) {
+          nxt = th;
+          found = true;
+        }
+      }
+      cells[c] = make_uint2(cnt, __float_as_uint(nxt));
+    }
+    __syncthreads();
+  }
   // quaternions of this lane's eight blocks (comparison transform only)
   float qa[8][4], qb[8][4];
   if constexpr (TF != kWht) {
@@ -171,7 +200,21 @@ void write_kernel(const void* __restrict__ keys, int64_t n,
 #pragma unroll
       for (int i = 0; i < 8; ++i) S[i] = P[i] * nrm;
       uint32_t words[BITS];
-      quantize_lane<BITS>(x, S, words);
+      if constexpr (BITS == 4) {
+        // the cell table where every key of the wave has a norm in
+        // [2^-100, 2^100] or 0 (thresholds and cell positions then keep full
+        // precision); the threshold search otherwise
+        const bool cells_ok = prm.cell_k > 0.0f &&
+            (nrm == 0.0f || (nrm >= 0x1p-100f && nrm <= 0x1p100f));
+        if (__builtin_amdgcn_ballot_w64(!cells_ok) == 0) {
+          const float kc = nrm > 0.0f ? prm.cell_k / nrm : 0.0f;
+          quantize_cells(x, kc, nrm, cells, words);
+        } else {
+          quantize_lane<BITS>(x, S, words);
+        }
+      } else {
+        quantize_lane<BITS>(x, S, words);
+      }
       // destination row: the key's own index, or its cache slot when appending
       int64_t row = key;
       bool store = valid;

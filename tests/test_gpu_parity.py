@@ -244,16 +244,19 @@ def test_query_magnitude_edges(G):
     assert torch.all(scores[0, 0] == 0), "a zero query must score exactly 0"
 
 
+@pytest.mark.parametrize("b", [3, 4])
 @pytest.mark.parametrize("d", [128, 512])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("scale", [1e-25, 1e-33, 1e25, 1e30])
-def test_tiny_and_huge_keys(scale, dtype, d):
+def test_tiny_and_huge_keys(scale, dtype, d, b):
     """Keys whose squared entries underflow or overflow fp32, mixed token by
     token with ordinary keys (both paths in one wave): the norm comes from
     the transformed coordinates, so indices, norms and scores meet the same
-    bounds as for any key."""
-    b, Hkv, G, T = 3, 2, 4, 700
-    rng = np.random.default_rng(int(abs(np.log10(scale))) + d + (scale > 1))
+    bounds as for any key.  At b = 4, norms outside [2^-100, 2^100] (the
+    1e-33 and 1e30 keys) take the threshold search instead of the cell
+    table, for their whole wave."""
+    Hkv, G, T = 2, 4, 700
+    rng = np.random.default_rng(int(abs(np.log10(scale))) + d + (scale > 1) + 1000 * (b - 3))
     k = rng.standard_normal((1, Hkv, T, d))
     k[:, :, ::2] *= scale
     keys = torch.from_numpy(k.astype(np.float32)).to(dtype)
@@ -262,6 +265,57 @@ def test_tiny_and_huge_keys(scale, dtype, d):
     label = f"keys at {scale:g} {dtype} d={d}"
     packed, norms = _write_and_check(keys, bits, b, label)
     _score_and_check(q, keys, packed, norms, bits, b, label)
+
+
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_b4_threshold_and_cell_sweep(d):
+    """4-bit quantizer: unit keys built so that their transformed
+    coordinates are chosen values (k = s * (H v) gives y = v for a unit v):
+    a dense sweep over +-3.2 sigma (every cell of the table in that range, a
+    few hundred points per cell), points at and within 1e-7..1e-3 of every
+    threshold on both sides, and basis keys (y = +-1, the table's ends).
+    Indices off by one are allowed only inside the boundary window."""
+    b, per_key = 4, 8
+    sigma = 1.0 / np.sqrt(d)
+    c, t = A.lloyd_max_codebook(d, b)
+    targets = list(np.linspace(-3.2 * sigma, 3.2 * sigma, 8192))
+    for th in t:
+        for off in (0.0, 1e-7, 3e-7, 1e-6, 2e-6, 1e-5, 1e-4, 1e-3):
+            targets += [th + off, th - off]
+    targets = np.array(targets)
+    rng = np.random.default_rng(900 + d)
+    rng.shuffle(targets)
+    nkeys = (len(targets) + per_key - 1) // per_key
+    v = np.zeros((nkeys + 2 * 4, d))
+    for i in range(nkeys):
+        pv = targets[i * per_key:(i + 1) * per_key]
+        pos = rng.choice(d, size=len(pv), replace=False)
+        rest = np.setdiff1d(np.arange(d), pos)
+        v[i, pos] = pv
+        v[i, rest] = np.sqrt((1.0 - np.sum(pv ** 2)) / len(rest)) * rng.choice([-1.0, 1.0], len(rest))
+    for j, col in enumerate((0, 1, d // 2, d - 1)):
+        v[nkeys + 2 * j, col] = 1.0
+        v[nkeys + 2 * j + 1, col] = -1.0
+    bits = W.sign_bits(d)
+    s = A.signs_from_bits(bits)
+    k = s * (v @ A.sylvester_hadamard(d))
+    keys = torch.from_numpy(k.astype(np.float32)).reshape(1, 1, -1, d)
+    m = axr()
+    packed, norms = m.quantize_keys(keys.to(DEV), bits, b)
+    torch.cuda.synchronize()
+    y, onorm = A.transform_keys(f64(keys.reshape(-1, d)), s)
+    assert np.max(np.abs(y - v)) < 1e-6
+    oidx = A.quantize(y, t)
+    gidx = A.unpack_indices(words_u32(packed.reshape(-1, d * b // 32)), d, b)
+    bad = gidx != oidx
+    if bad.any():
+        dist = np.min(np.abs(y[bad][:, None] - t[None, :]), axis=1)
+        assert dist.max() < 1e-6, f"d={d}: index off {dist.max():.3e} from any threshold"
+        assert np.all(np.abs(gidx[bad] - oidx[bad]) == 1)
+    far = np.min(np.abs(y[..., None] - t), axis=-1) >= 1e-6
+    assert far.sum() > 0.9 * far.size
+    assert np.array_equal(gidx[far], oidx[far])
+    assert_norms(f64(norms.reshape(-1)), onorm, f"sweep d={d}")
 
 
 def test_score_is_deterministic_and_tile_independent():
