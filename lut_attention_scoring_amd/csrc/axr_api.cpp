@@ -10,7 +10,10 @@
 #include <cstdio>
 #include <climits>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <tuple>
 
 #include "axr_internal.h"
 
@@ -114,6 +117,17 @@ static float cell_scale(const float* tpos, int half, double zmax) {
   return 0.0f;   // no scale found: the kernel keeps its threshold search
 }
 
+// cell_scale for (d, b, transform), computed once per process (thread-safe).
+static float cached_cell_scale(int d, int b, int tf, const float* tpos, int half, double zmax) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int>, float> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(d, b, tf);
+  auto it = cache.find(key);
+  if (it == cache.end()) it = cache.emplace(key, cell_scale(tpos, half, zmax)).first;
+  return it->second;
+}
+
 // Write-kernel parameters: sign words and the positive thresholds scaled by
 // sqrt(d) (the kernel compares against them times the key's norm).
 // (The block-quaternion transform is orthonormal as it stands, so there the
@@ -128,7 +142,8 @@ static axr::WriteParams write_params(const uint32_t* sign_bits, int d, int b,
   const double sqrt_d = tf == axr::kWht ? std::sqrt(static_cast<double>(d)) : 1.0;
   for (int i = 0; i + 1 < half; ++i) p.tpos[i] = static_cast<float>(cb.threshold[half + i] * sqrt_d);
   p.inv_sqrt_d = static_cast<float>(1.0 / sqrt_d);
-  p.cell_k = b == 4 ? cell_scale(p.tpos, half, tf == axr::kWht ? sqrt_d : 1.0) : 0.0f;
+  p.cell_k = b == 4 ? cached_cell_scale(d, b, tf, p.tpos, half, tf == axr::kWht ? sqrt_d : 1.0)
+                   : 0.0f;
   p.t_cap = 0;
   p.Hkv = 1;
   return p;
