@@ -69,7 +69,6 @@ __device__ __forceinline__ void quat_block(float* v, const float (&a)[4], const 
   }
 }
 
-
 // Waves per SIMD the compiler is asked to fit: 6 (at most 80 VGPRs) for the
 // fp16 d = 128 Hadamard kernels with 2 or 3 bits, which would otherwise take
 // 81-82 VGPRs and run 5 waves per SIMD; the other instances already fit 6
@@ -83,12 +82,11 @@ constexpr int write_waves() {
 // TF selects the transform: kWht (sign pattern + Walsh-Hadamard), or the
 // block-quaternion comparison transforms kIsoFull / kIsoFast.
 template <int D, int BITS, int DT, int TF>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(write_waves<D, BITS, DT, TF>())))
-void write_kernel(const void* __restrict__ keys, int64_t n,
-                                                     WriteParams prm,
-                                                     uint32_t* __restrict__ packed,
-                                                     float* __restrict__ norms,
-                                                     float* __restrict__ yout, int mode) {
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(write_waves<D, BITS, DT, TF>())))
+void write_kernel(const void* __restrict__ keys, int64_t n, WriteParams prm,
+                  uint32_t* __restrict__ packed, float* __restrict__ norms,
+                  float* __restrict__ yout, int mode) {
   constexpr int LPK = D / 32;
   constexpr int KPB = kBlock / LPK;
   constexpr int W = D * BITS / 32;
