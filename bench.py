@@ -37,7 +37,7 @@ CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
 # files below); otherwise traffic is reported as null.
 COUNTER_TRAFFIC = {
     "write": {"sources": ["axr_write.hip", "axr_keyquant.h", "axr_device.h", "axr_internal.h"],
-              "sha1": "5c6204dc4b2efbc13345d86c9ebba077529bde83",
+              "sha1": "fb9d2b6f897ea1fac17492de7689ee757b947702",
               "bytes": (262196.1 * 2.0 + 106531.1) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
               "sha1": "9d40cc3e216f11a072404deb3886f0ec983099bd",

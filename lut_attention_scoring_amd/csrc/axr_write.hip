@@ -205,8 +205,8 @@ void write_kernel(const void* __restrict__ keys, int64_t n, WriteParams prm,
         const bool cells_ok = prm.cell_k > 0.0f &&
             (nrm == 0.0f || (nrm >= 0x1p-100f && nrm <= 0x1p100f));
         if (__builtin_amdgcn_ballot_w64(!cells_ok) == 0) {
-          const float kc = nrm > 0.0f ? prm.cell_k / nrm : 0.0f;
-          quantize_cells(x, kc, nrm, cells, words);
+          const float cells_per_z = nrm > 0.0f ? prm.cell_k / nrm : 0.0f;
+          quantize_cells(x, cells_per_z, nrm, cells, words);
         } else {
           quantize_lane<BITS>(x, S, words);
         }
