@@ -99,10 +99,11 @@ int axr_quantize_keys(const void* keys, int dtype, int64_t n, int d, int b,
  *   q' = H_d (s * q[bi][h]) / sqrt(d)                 (queries not normalised)
  *   LUT[j][c] = q'_j * centroid_c
  *   scores[bi][h][t] = norms[r] * sum_j LUT[j][idx_j(r)],  r = (bi*Hkv + kvh)*t_cap + t
- * The sum is taken exactly in 32-bit fixed point over pairs of coordinates
- * (a table entry holds two coordinates' products); the only roundings are the
- * table entries (relative 2^-30 of the head's full scale) and the final fp32
- * products, far inside 1e-5 of norms * sum_j |LUT[j][idx_j]|.
+ * The sum is taken exactly in 32-bit fixed point over table entries that
+ * each hold the products of two coordinates (one coordinate at b = 4, whose
+ * pair table would not fit in LDS); the only roundings are the table entries
+ * (relative 2^-30 of the head's full scale) and the final fp32 products, far
+ * inside 1e-5 of norms * sum_j |LUT[j][idx_j]|.
  *   q       : device, [B][Hq][d] of q_dtype, 16-byte aligned
  *   packed  : device uint32, [B][Hkv][t_cap][W] as written by axr_quantize_keys
  *   norms   : device float, [B][Hkv][t_cap]
