@@ -109,3 +109,38 @@ def test_empty_inputs():
     assert w["packed"].shape == (1, 1, 0, 2)
     sc = A.read_path(np.ones((1, 2, d)), w["packed"], w["norms"], s, b)
     assert sc.shape == (1, 2, 0)
+
+
+def test_score_condition_pins():
+    """The tolerance scale ||k|| sum_j |q'_j c_idx_j|: a loop over every term
+    (GQA head h reads KV head h // G), no smaller than |score| (triangle
+    inequality), and equal to the score when every term is nonnegative."""
+    keys, q, bits, b = _case(31, B=2, Hkv=2, G=2, T=5, d=32, b=3)
+    s = A.signs_from_bits(bits)
+    w = A.write_path(keys, s, b)
+    c, _ = A.lloyd_max_codebook(32, b)
+    qp = A.transform_queries(q, s)
+    cond = A.score_condition(qp, w["idx"], w["norms"], c)
+    B_, Hq, d = qp.shape
+    G = Hq // w["idx"].shape[1]
+    for bi in range(B_):
+        for h in range(Hq):
+            for t in range(w["idx"].shape[2]):
+                kv = h // G
+                terms = [abs(qp[bi, h, j] * c[w["idx"][bi, kv, t, j]]) for j in range(d)]
+                assert cond[bi, h, t] == pytest.approx(w["norms"][bi, kv, t] * sum(terms),
+                                                       rel=1e-13)
+    score = A.read_path(q, w["packed"], w["norms"], s, b)
+    assert np.all(np.abs(score) <= cond * (1 + 1e-13))
+    # nonnegative terms: q' >= 0 and every index in the positive half
+    idx_pos = np.full_like(w["idx"], (1 << b) - 1)
+    qp_pos = np.abs(qp)
+    lut = A.build_lut(qp_pos, c)
+    direct = np.empty_like(cond)
+    for bi in range(B_):
+        for h in range(Hq):
+            kv = h // G
+            direct[bi, h] = w["norms"][bi, kv] * lut[bi, h][np.arange(d), idx_pos[bi, kv]].sum(-1)
+    np.testing.assert_allclose(A.score_condition(qp_pos, idx_pos, w["norms"], c), direct,
+                               rtol=1e-13)
+    assert np.all(direct > 0)
