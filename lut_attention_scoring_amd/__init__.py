@@ -140,6 +140,17 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DTYPES[t.dtype]
 
 
+def _need_dtype(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _need_out(t: torch.Tensor, shape, dtype, name: str):
+    _need_dtype(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _need_cuda(*tensors):
     for t in tensors:
         if not t.is_cuda:
@@ -163,6 +174,8 @@ def quantize_keys(keys: torch.Tensor, sign_bits, b: int, packed: torch.Tensor = 
         packed = torch.empty(*lead, packed_words(d, b), dtype=torch.int32, device=keys.device)
     if norms is None:
         norms = torch.empty(*lead, dtype=torch.float32, device=keys.device)
+    _need_dtype(packed, torch.int32, "packed")
+    _need_dtype(norms, torch.float32, "norms")
     _need_cuda(keys, packed, norms)
     n = keys.numel() // d if d else 0
     if packed.numel() != n * packed_words(d, b) or norms.numel() != n:
@@ -184,6 +197,8 @@ def append_keys(keys: torch.Tensor, sign_bits, b: int, packed: torch.Tensor,
         raise ValueError("keys, packed and norms shapes disagree")
     if pos.dtype != torch.int32 or tuple(pos.shape) != (B,):
         raise ValueError("pos must be an int32 tensor of shape [B]")
+    _need_dtype(packed, torch.int32, "packed")
+    _need_dtype(norms, torch.float32, "norms")
     _need_cuda(keys, packed, norms, pos)
     words, wp = _words_ptr(sign_words(sign_bits))
     _check(lib.axr_append_keys(keys.data_ptr(), _dtype_code(keys), B, Hkv, d, b, wp,
@@ -208,9 +223,10 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, sign_bits, b: int, packed:
     T = t_cap if T is None else int(T)
     if out is None:
         out = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    _need_dtype(packed, torch.int32, "packed")
+    _need_dtype(norms, torch.float32, "norms")
+    _need_out(out, (B, Hq, T), torch.float32, "out")
     _need_cuda(q, k_new, packed, norms, pos, out)
-    if tuple(out.shape) != (B, Hq, T):
-        raise ValueError("out has the wrong shape")
     words, wp = _words_ptr(sign_words(sign_bits))
     _check(lib.axr_decode_step(q.data_ptr(), _dtype_code(q), k_new.data_ptr(),
                                _dtype_code(k_new), wp, pos.data_ptr(), B, Hq, Hkv, T, t_cap, d,
@@ -232,9 +248,10 @@ def score(q: torch.Tensor, packed: torch.Tensor, norms: torch.Tensor, sign_bits,
     T = t_cap if T is None else int(T)
     if out is None:
         out = torch.empty(B, Hq, T, dtype=torch.float32, device=q.device)
+    _need_dtype(packed, torch.int32, "packed")
+    _need_dtype(norms, torch.float32, "norms")
+    _need_out(out, (B, Hq, T), torch.float32, "out")
     _need_cuda(q, packed, norms, out)
-    if tuple(out.shape) != (B, Hq, T):
-        raise ValueError("out has the wrong shape")
     words, wp = _words_ptr(sign_words(sign_bits))
     if lens is None:
         _check(lib.axr_score(q.data_ptr(), _dtype_code(q), packed.data_ptr(), norms.data_ptr(),
@@ -276,9 +293,11 @@ def score_softmax(q: torch.Tensor, packed: torch.Tensor, norms: torch.Tensor, si
     need = score_softmax_workspace_bytes(B, Hq, Hkv, T, d, b)
     if workspace is None:
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=q.device)
+    _need_dtype(packed, torch.int32, "packed")
+    _need_dtype(norms, torch.float32, "norms")
+    _need_out(out, (B, Hq, T), torch.float32, "out")
+    _need_out(lse, (B, Hq), torch.float32, "lse")
     _need_cuda(q, packed, norms, out, lse, workspace)
-    if tuple(out.shape) != (B, Hq, T) or tuple(lse.shape) != (B, Hq):
-        raise ValueError("out or lse has the wrong shape")
     if lens is not None:
         if lens.dtype != torch.int32 or tuple(lens.shape) != (B,):
             raise ValueError("lens must be an int32 tensor of shape [B]")
@@ -346,6 +365,8 @@ def quantize_keys_isoquant(keys: torch.Tensor, quats: torch.Tensor, b: int, full
         packed = torch.empty(*lead, packed_words(d, b), dtype=torch.int32, device=keys.device)
     if norms is None:
         norms = torch.empty(*lead, dtype=torch.float32, device=keys.device)
+    _need_dtype(packed, torch.int32, "packed")
+    _need_dtype(norms, torch.float32, "norms")
     _need_cuda(keys, packed, norms, quats)
     n = keys.numel() // d if d else 0
     if packed.numel() != n * packed_words(d, b) or norms.numel() != n:
@@ -364,6 +385,7 @@ def transform_isoquant(x: torch.Tensor, quats: torch.Tensor, full: bool = True,
     quats = _quats(quats, d, x.device)
     if out is None:
         out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _need_out(out, x.shape, torch.float32, "out")
     _need_cuda(x, out, quats)
     n = x.numel() // d if d else 0
     _check(lib.axr_transform_isoquant(x.data_ptr(), _dtype_code(x), n, d, quats.data_ptr(),
@@ -377,6 +399,7 @@ def transform(x: torch.Tensor, sign_bits, normalize: bool = True, out: torch.Ten
     d = x.shape[-1]
     if out is None:
         out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _need_out(out, x.shape, torch.float32, "out")
     _need_cuda(x, out)
     n = x.numel() // d if d else 0
     words, wp = _words_ptr(sign_words(sign_bits))
@@ -387,18 +410,20 @@ def transform(x: torch.Tensor, sign_bits, normalize: bool = True, out: torch.Ten
 
 def probe_read_stream(buf: torch.Tensor, sink: torch.Tensor, nbytes: int = None):
     """Bandwidth probe (include/axr_probe.h): stream-read `nbytes` of `buf`."""
-    _need_cuda(buf, sink)
     nbytes = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    if nbytes > buf.numel() * buf.element_size() or sink.numel() * sink.element_size() < 4:
+        raise ValueError("probe size exceeds the buffer, or the sink is under 4 bytes")
+    _need_cuda(buf, sink)
     if lib.axr_probe_read_stream(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(buf)) != 0:
         raise AxrError(EINVAL, "axr_probe_read_stream rejected its arguments")
 
 
 def probe_read_write(src: torch.Tensor, in_bytes: int, dst: torch.Tensor, out_bytes: int):
     """Bandwidth probe: read `in_bytes` of `src`, write `out_bytes` of `dst`."""
-    _need_cuda(src, dst)
     if (in_bytes > src.numel() * src.element_size()
             or out_bytes > dst.numel() * dst.element_size()):
         raise ValueError("probe sizes exceed the buffers")
+    _need_cuda(src, dst)
     if lib.axr_probe_read_write(src.data_ptr(), int(in_bytes), dst.data_ptr(), int(out_bytes),
                                 _stream(src)) != 0:
         raise AxrError(EINVAL, "axr_probe_read_write rejected its arguments")
