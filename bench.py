@@ -40,7 +40,7 @@ COUNTER_TRAFFIC = {
               "sha1": "fb9d2b6f897ea1fac17492de7689ee757b947702",
               "bytes": (262196.1 * 2.0 + 106531.1) * 1024},
     "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "9d40cc3e216f11a072404deb3886f0ec983099bd",
+              "sha1": "fee22021ac8518faff9cdd4adecb29aa7743c683",
               "bytes": (53432.2 * 2.0 + 34485.5) * 1024},
 }
 

@@ -161,7 +161,9 @@ int axr_score_ragged(const void* q, int q_dtype, const uint32_t* packed, const f
  * the cache and scores it from the fresh record.
  *   k_new : device [B][Hkv][d] of k_dtype, 4-byte aligned
  *   pos   : device int32 [B]; a slot outside [0, t_cap) appends nothing and
- *           row bi is scored for t < min(max(pos[bi] + 1, 0), T)
+ *           row bi is scored for t < min(max(pos[bi] + 1, 0), T); a slot in
+ *           [T, t_cap) is appended (by the row's last tile) but not scored,
+ *           and with T = 0 the call is the append alone
  *   packed, norms : the cache, as for axr_append_keys (in/out)
  *   scores: device float [B][Hq][T]; entries past a row's length are not written
  * Same requirements and errors as axr_score.

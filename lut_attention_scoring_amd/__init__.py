@@ -211,7 +211,8 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, sign_bits, b: int, packed:
                 norms: torch.Tensor, pos: torch.Tensor, T: int = None, out: torch.Tensor = None):
     """One decode step in one launch: k_new [B, Hkv, d] quantized into slot
     pos[bi] of the cache and q [B, Hq, d] scored over t < pos[bi] + 1
-    -> scores fp32 [B, Hq, T] (T defaults to t_cap)."""
+    -> scores fp32 [B, Hq, T] (T defaults to t_cap).  A slot in [T, t_cap)
+    is stored but not scored."""
     B, Hq, d = q.shape
     Bc, Hkv, t_cap, W = packed.shape
     if Bc != B or W != packed_words(d, b) or tuple(norms.shape) != (B, Hkv, t_cap):

@@ -443,7 +443,12 @@ int axr_decode_step(const void* q, int q_dtype, const void* k_new, int k_dtype,
   int rc = check_score_sizes(d, b, q_dtype, sign_bits, B, Hq, Hkv, T, t_cap);
   if (rc != AXR_OK) return rc;
   if (!supported_dtype(k_dtype)) return fail(AXR_EUNSUPPORTED, "k_dtype=%d is not supported", k_dtype);
-  if (B == 0 || T == 0) return ok();
+  if (B == 0) return ok();
+  if (T == 0) {                                 // nothing to score: the append alone
+    if (t_cap == 0) return ok();
+    return axr_append_keys(k_new, k_dtype, B, Hkv, d, b, sign_bits, pos, t_cap, packed, norms,
+                           stream);
+  }
   if (q == nullptr || k_new == nullptr || pos == nullptr || packed == nullptr ||
       norms == nullptr || scores == nullptr)
     return fail(AXR_EINVAL, "q, k_new, pos, packed, norms and scores must be non-null");

@@ -247,6 +247,11 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   const size_t rowbase = static_cast<size_t>(row) * prm.t_cap;
   // block-uniform: this tile holds the decode step's new token
   const bool holds_new = MODE == kDecode && slot >= t0 && slot < t1;
+  // a new token at or past T but inside the cache is scored by no tile; the
+  // first head group's block of the row's last tile stores it
+  const bool tail_new = MODE == kDecode && slot >= prm.T && slot < prm.t_cap &&
+                        tile == prm.tiles - 1 && hg == 0;
+  const bool makes_new = holds_new || tail_new;
   __shared__ uint8_t nidx[D];                   // its indices, then its record
   __shared__ uint32_t newrec[S::W];
   __shared__ float newnrm;
@@ -356,7 +361,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   // rule (sign pattern, Walsh-Hadamard transform, index = number of
   // thresholds below z, a zero key in the cell below 0), lane l holding
   // coordinates l + 64 r; indices go to LDS for packing below.
-  if (MODE == kDecode && holds_new && wave == NTHREADS / 64 - 1) {
+  if (MODE == kDecode && makes_new && wave == NTHREADS / 64 - 1) {
     const size_t krow = (static_cast<size_t>(bi) * prm.Hkv + kvh) * D + lane;
     float kv[R];
     float ss = 0.0f;
@@ -411,7 +416,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 
   // ... and packs them into the record: thread i of the last wave assembles
   // word i; the first head group's block also stores record and norm.
-  if (MODE == kDecode && holds_new && tid >= NTHREADS - S::W) {
+  if (MODE == kDecode && makes_new && tid >= NTHREADS - S::W) {
     const int wi = tid - (NTHREADS - S::W);
     uint32_t word = 0u;
     for (int j = (32 * wi) / BITS; j <= (32 * wi + 31) / BITS && j < D; ++j) {

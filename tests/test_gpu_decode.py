@@ -249,8 +249,8 @@ def test_fused_decode_step(d, b, G, dtype):
     m = axr()
     rng = np.random.default_rng(5000 + d + 10 * b + G)
     Hkv, t_cap, T = 2, 2100, 2000
-    pos = [0, 1999, 777, -1, 2050, 255, 256, 1023]        # tile edges, -1, past T, past t_cap
-    pos[4] = t_cap + 3
+    # tile edges, -1, past T inside the cache, past t_cap
+    pos = [0, 1999, 777, -1, 2050, 255, 256, 1023, t_cap + 3]
     B = len(pos)
     bits = W.sign_bits(d)
     cache = _keys(rng, (B, Hkv, t_cap, d), dtype)
@@ -265,7 +265,7 @@ def test_fused_decode_step(d, b, G, dtype):
     torch.cuda.synchronize()
     label = f"fused d={d} b={b} G={G}"
     # appended records against the oracle's write of the new keys; all else untouched
-    assert _check_appended(new, packed, norms, pos, bits, b, label) == 6
+    assert _check_appended(new, packed, norms, pos, bits, b, label) == 7
     _untouched(before_p, before_n, words_u32(packed), norms.cpu().numpy(), pos)
     # scores given the GPU's (new) records
     keys_now = cache.clone()
@@ -286,6 +286,80 @@ def test_fused_decode_step(d, b, G, dtype):
         gidx = A.unpack_indices(words_u32(packed[bi:bi + 1, :, tt]), d, b)
         onorm = A.key_norms(f64(keys_now[bi:bi + 1, :, tt]))
         assert_scores(got[bi:bi + 1, :, toks], qprime[bi:bi + 1], gidx, onorm, c,
+                      f"{label} bi={bi}")
+
+
+def test_fused_decode_step_with_nothing_to_score():
+    """T = 0: the fused step is the append alone (slots in and out of the
+    cache), and the cache equals the one the write path's append gives."""
+    m = axr()
+    rng = np.random.default_rng(6100)
+    d, b, Hkv, G, t_cap = 128, 3, 2, 4, 50
+    pos = [0, 49, 50, -1, 17]
+    B = len(pos)
+    bits = W.sign_bits(d)
+    cache = _keys(rng, (B, Hkv, t_cap, d), torch.float16)
+    new = _keys(rng, (B, Hkv, d), torch.float16, scale=4.0)
+    q = _keys(rng, (B, Hkv * G, d), torch.float16, scale=1.0)
+    pos_t = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    packed, norms = m.quantize_keys(cache.to(DEV), bits, b)
+    ref_p, ref_n = packed.clone(), norms.clone()
+    m.append_keys(new.to(DEV), bits, b, ref_p, ref_n, pos_t)
+    out = torch.empty(B, Hkv * G, 0, device=DEV)
+    m.decode_step(q.to(DEV), new.to(DEV), bits, b, packed, norms, pos_t, T=0, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(packed, ref_p) and torch.equal(norms, ref_n)
+    assert _check_appended(new, packed, norms, pos, bits, b, "fused T=0") == 3
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_fused_decode_step_random(i):
+    """The fused decode step on seeded random shapes: d, b, key dtype, KV
+    heads, group size, t_cap >= T and slots anywhere in [-3, t_cap + 3)."""
+    m = axr()
+    rng = np.random.default_rng(7000 + i)
+    d = int(rng.choice([128, 256, 512]))
+    b = int(rng.integers(2, 5))
+    dtype = [torch.float32, torch.float16, torch.bfloat16][int(rng.integers(0, 3))]
+    Hkv = int(rng.integers(1, 4))
+    G = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16]))
+    t_cap = int(rng.integers(1, 1500))
+    T = int(rng.integers(1, t_cap + 1))
+    B = int(rng.integers(1, 6))
+    pos = [int(v) for v in rng.integers(-3, t_cap + 3, size=B)]
+    label = f"fused random {i}: d={d} b={b} {dtype} Hkv={Hkv} G={G} t_cap={t_cap} T={T} pos={pos}"
+    print(label, flush=True)
+    bits = W.sign_bits(d)
+    cache = _keys(rng, (B, Hkv, t_cap, d), dtype)
+    packed, norms = m.quantize_keys(cache.to(DEV), bits, b)
+    new = _keys(rng, (B, Hkv, d), dtype, scale=4.0)
+    q = _keys(rng, (B, Hkv * G, d), dtype, scale=1.0)
+    out = torch.full((B, Hkv * G, T), SENTINEL, device=DEV)
+    torch.cuda.synchronize()
+    before_p, before_n = words_u32(packed).copy(), norms.cpu().numpy().copy()
+    m.decode_step(q.to(DEV), new.to(DEV), bits, b, packed, norms,
+                  torch.tensor(pos, dtype=torch.int32, device=DEV), T=T, out=out)
+    torch.cuda.synchronize()
+    n_app = sum(1 for p_ in pos if 0 <= p_ < t_cap)
+    assert _check_appended(new, packed, norms, pos, bits, b, label) == n_app
+    _untouched(before_p, before_n, words_u32(packed), norms.cpu().numpy(), pos)
+    keys_now = cache.clone()
+    for bi, slot in enumerate(pos):
+        if 0 <= slot < t_cap:
+            keys_now[bi, :, slot] = new[bi]
+    s = A.signs_from_bits(bits)
+    c, _ = A.lloyd_max_codebook(d, b)
+    qprime = A.transform_queries(f64(q), s)
+    got = f64(out)
+    for bi, slot in enumerate(pos):
+        n_tok = min(max(slot + 1, 0), T)
+        assert np.all(got[bi, :, n_tok:] == SENTINEL), f"{label} bi={bi} wrote past its length"
+        if n_tok == 0:
+            continue
+        tt = torch.arange(n_tok)
+        gidx = A.unpack_indices(words_u32(packed[bi:bi + 1, :, tt]), d, b)
+        onorm = A.key_norms(f64(keys_now[bi:bi + 1, :, tt]))
+        assert_scores(got[bi:bi + 1, :, :n_tok], qprime[bi:bi + 1], gidx, onorm, c,
                       f"{label} bi={bi}")
 
 
