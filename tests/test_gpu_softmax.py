@@ -124,3 +124,23 @@ def test_softmax_llama_full_size_sampled_rows():
         cond = A.score_condition(qp, gidx, onorm, c)[0]
         assert_softmax(f64(probs[bi, h:h + 1]), f64(lse[bi, h:h + 1]), ref, cond, scale, T,
                        f"llama row ({bi}, {h})")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_softmax_random_shapes(i):
+    """Seeded random shapes: d, b, key dtype, KV heads, group sizes with padded
+    head slots, t_cap >= T, lengths anywhere in [-2, T + 40], scales."""
+    rng = np.random.default_rng(8000 + i)
+    d = int(rng.choice([128, 256, 512]))
+    b = int(rng.integers(2, 5))
+    G = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16]))
+    Hkv = int(rng.integers(1, 4))
+    T = int(rng.integers(1, 2500 if d < 512 else 1200))
+    t_cap = T + int(rng.integers(0, 60))
+    B = int(rng.integers(1, 5))
+    lens = [int(v) for v in rng.integers(-2, T + 40, size=B)]
+    dtype = [torch.float32, torch.float16, torch.bfloat16][int(rng.integers(0, 3))]
+    scale = float(rng.choice([1.0 / math.sqrt(d), 0.3, 1.0]))
+    print(f"softmax random {i}: d={d} b={b} G={G} Hkv={Hkv} T={T} t_cap={t_cap} lens={lens} "
+          f"{dtype} scale={scale}", flush=True)
+    _run(d, b, G, lens, T=T, t_cap=t_cap, scale=scale, seed=9000 + i, Hkv=Hkv, dtype=dtype)
