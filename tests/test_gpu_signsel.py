@@ -108,3 +108,27 @@ def test_selection_full_calibration_set():
     assert idx == int(np.argmin(objective))
     worst = int(np.argmax(objective))
     _check(cal["keys"], cal["q"], cands, 4, sorted({0, idx, worst}), "full")
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_selection_errors_random_shapes(i):
+    """Seeded random shapes of the selection inputs: samples, batch, KV heads,
+    group size, tokens, d, b, dtypes; every candidate's sums against the
+    oracle's from the GPU's own indices."""
+    rng = np.random.default_rng(9500 + i)
+    S = int(rng.integers(1, 4))
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.integers(1, 3))
+    G = int(rng.choice([1, 2, 3, 4, 8]))
+    T = int(rng.integers(1, 900))
+    d = int(rng.choice([128, 256]))
+    b = int(rng.integers(2, 5))
+    dtype = [torch.float32, torch.float16, torch.bfloat16][int(rng.integers(0, 3))]
+    C = int(rng.integers(1, 4))
+    label = f"selection random {i}: S={S} B={B} Hkv={Hkv} G={G} T={T} d={d} b={b} {dtype} C={C}"
+    print(label, flush=True)
+    keys = torch.from_numpy((rng.standard_normal((S, B, Hkv, T, d)) * np.exp(
+        rng.standard_normal(d)) + 0.3).astype(np.float32)).to(dtype)
+    q = torch.from_numpy(rng.standard_normal((S, B, Hkv * G, d)).astype(np.float32)).to(dtype)
+    cands = rng.integers(0, 2, size=(C, d)).astype(np.uint8)
+    _check(keys, q, cands, b, range(C), label)
