@@ -91,6 +91,34 @@ def test_append_into_slots(d, b, dtype):
     _untouched(before_p, before_n, after_p, after_n, pos)
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_append_random_shapes(i):
+    """Appends with seeded random batch and KV-head counts (up to several
+    blocks of keys), cache lengths and slots anywhere in [-3, t_cap + 3)."""
+    m = axr()
+    rng = np.random.default_rng(7500 + i)
+    d = int(rng.choice([128, 256, 512]))
+    b = int(rng.integers(2, 5))
+    dtype = [torch.float32, torch.float16, torch.bfloat16][int(rng.integers(0, 3))]
+    B = int(rng.integers(1, 41))
+    Hkv = int(rng.integers(1, 9))
+    t_cap = int(rng.integers(1, 64))
+    pos = [int(v) for v in rng.integers(-3, t_cap + 3, size=B)]
+    label = f"append random {i}: d={d} b={b} {dtype} B={B} Hkv={Hkv} t_cap={t_cap}"
+    bits = W.sign_bits(d)
+    cache = _keys(rng, (B, Hkv, t_cap, d), dtype)
+    packed, norms = m.quantize_keys(cache.to(DEV), bits, b)
+    new = _keys(rng, (B, Hkv, d), dtype, scale=5.0)
+    torch.cuda.synchronize()
+    before_p, before_n = words_u32(packed).copy(), norms.cpu().numpy().copy()
+    m.append_keys(new.to(DEV), bits, b, packed, norms,
+                  torch.tensor(pos, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    n_app = sum(1 for p_ in pos if 0 <= p_ < t_cap)
+    assert _check_appended(new, packed, norms, pos, bits, b, label) == n_app
+    _untouched(before_p, before_n, words_u32(packed), norms.cpu().numpy(), pos)
+
+
 def test_append_zero_key_and_exact_ties():
     # a zero key takes the cell below 0 everywhere; its norm is 0
     m = axr()
