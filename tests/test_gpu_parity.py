@@ -318,6 +318,22 @@ def test_b4_threshold_and_cell_sweep(d):
     assert_norms(f64(norms.reshape(-1)), onorm, f"sweep d={d}")
 
 
+@pytest.mark.parametrize("d, b, G", [(128, 3, 64), (128, 3, 63), (128, 4, 40), (256, 3, 64),
+                                     (512, 2, 33)])
+def test_score_largest_groups(d, b, G):
+    """Group sizes up to the supported 64 query heads per KV head, including
+    ones that leave padded head slots in the last head group of a block."""
+    rng = np.random.default_rng(6600 + d + b + G)
+    Hkv, T = 2, 700
+    keys = torch.from_numpy(rng.standard_normal((1, Hkv, T, d)).astype(np.float32)).to(
+        torch.float16)
+    q = torch.from_numpy(rng.standard_normal((1, Hkv * G, d)).astype(np.float32))
+    bits = W.sign_bits(d)
+    label = f"groups d={d} b={b} G={G}"
+    packed, norms = _write_and_check(keys, bits, b, label)
+    _score_and_check(q, keys, packed, norms, bits, b, label)
+
+
 def test_score_is_deterministic_and_tile_independent():
     m = axr()
     w = W.llama_decode(B=1, Hkv=2, Hq=8, T=5000)
