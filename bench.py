@@ -444,6 +444,7 @@ def main():
                       "bytes_per_key": write_bytes_per_key,
                       "traffic": counter_traffic("write")},
             "score": {"ms": score_ms, "keys_per_s": n / (score_ms * 1e-3),
+                      "head_scores_per_s": n * (Hq // Hkv) / (score_ms * 1e-3),
                       "GB_per_s": score_gbs, "frac_hbm": score_gbs / HBM_PEAK_GBS,
                       "bytes_per_key": score_bytes_per_key,
                       "traffic": counter_traffic("score")},
