@@ -285,7 +285,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   //    holds coordinates l + 64 r; butterflies over r in registers and over
   //    the lane bits by cross-lane exchange.  The same wave sums |q'_j| (in a
   //    fixed order, so every block of a row gets the same scale) and picks
-  //    the head's fixed-point scale 2^e with sum_j |q'_j| max|c| 2^e < 2^30.
+  //    the head's fixed-point scale 2^e with sum_j |q'_j| max|c| 2^e < 2^31:
+  //    the sum of a key's table entries then fits int32 (with at most d/2 of
+  //    rounding on top, far below the 1e-4 relative slack of the bound), and
+  //    the 32-bit sums, which wrap, end exact.
   constexpr int R = D / 64;
   float v[R];
   if (wave < GB) {
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
       const float f = sa * cmax * 1.0001f;
       int e = 0;
       if (f > 0.0f) frexpf(f, &e);              // f < 2^e
-      int sh = 30 - e;
+      int sh = 31 - e;
       // up to 2^252 for tiny queries, applied as two powers of two that are
       // each representable (the second is 1 unless sh > 126)
       sh = sh > 252 ? 252 : (sh < -126 ? -126 : sh);
