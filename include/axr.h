@@ -215,8 +215,8 @@ int axr_score_softmax(const void* q, int q_dtype, const uint32_t* packed, const 
  *   errors[(c*S + i)*2 + 0] = sum (s_lut - s_exact)^2
  *   errors[(c*S + i)*2 + 1] = sum s_exact^2
  * over every (batch, query head, token) of the sample, accumulated in fp64
- * (s_exact = q . k in fp32).  The caller picks, e.g., the candidate whose
- * worst sample has the smallest sqrt(err / ref).
+ * (s_exact = q . k in fp32).  axr_sign_selection_choose turns these sums into
+ * the choice.
  *   keys      : device [S][B][Hkv][T][d] of `dtype`, 16-byte aligned
  *   q         : device [S][B][Hq][d] of `q_dtype`, 16-byte aligned
  *   errors    : device double [C][S][2], 8-byte aligned
@@ -231,6 +231,26 @@ int axr_sign_selection_errors(const void* keys, int dtype, const void* q, int q_
                               int B, int Hq, int Hkv, int64_t T, int d, int b,
                               const uint32_t* candidates, int C, double* errors,
                               void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Choice rule of the sign-pattern selection (AXELRAM, Abstract: the pattern
+ * is chosen once, gradient-free, from the candidates' results on the
+ * calibration samples).  Host only, no HIP call.  For candidate c the
+ * objective is its worst sample's relative score error,
+ *   objective[c] = max_i sqrt(err_ci / ref_ci),
+ *   err_ci = errors[(c*S + i)*2 + 0],  ref_ci = errors[(c*S + i)*2 + 1],
+ * where a sample with ref_ci = 0 (no exact score mass, e.g. a zero query)
+ * counts 0 if err_ci = 0 and +inf otherwise; *index receives the candidate
+ * with the smallest objective, the first one on ties.
+ *   errors    : HOST double [C][S][2], as axr_sign_selection_errors writes them
+ *               (copied to the host by the caller)
+ *   index     : HOST int (output)
+ *   objective : HOST double [C] (output), or NULL
+ * Errors: AXR_EINVAL for C < 1, S < 1, a null errors or index pointer, or a
+ * negative or NaN sum (nothing is written then).
+ */
+int axr_sign_selection_choose(const double* errors, int C, int S, int* index,
+                              double* objective);
 
 /*
  * Comparison write path with block-quaternion rotations in place of the sign

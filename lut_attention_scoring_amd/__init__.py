@@ -20,9 +20,8 @@ import torch
 __all__ = [
     "AxrError", "LIB_PATH", "lib", "version", "codebook", "sign_words",
     "packed_words", "quantize_keys", "append_keys", "decode_step", "score", "score_softmax",
-    "transform",
-    "sign_selection_errors", "select_sign_pattern", "quantize_keys_isoquant",
-    "transform_isoquant",
+    "transform", "sign_selection_errors", "sign_selection_choose", "select_sign_pattern",
+    "quantize_keys_isoquant", "transform_isoquant",
     "probe_read_stream",
     "probe_read_write",
     "F32", "F16", "BF16",
@@ -80,6 +79,8 @@ def _load():
     so.axr_sign_selection_errors.restype = i32
     so.axr_sign_selection_errors.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i64, i32, i32,
                                              u32p, i32, vp, vp, i64, vp]
+    so.axr_sign_selection_choose.restype = i32
+    so.axr_sign_selection_choose.argtypes = [dp, i32, i32, ctypes.POINTER(ctypes.c_int), dp]
     so.axr_quantize_keys_isoquant.restype = i32
     so.axr_quantize_keys_isoquant.argtypes = [vp, i32, i64, i32, i32, vp, i32, vp, vp, vp]
     so.axr_transform_isoquant.restype = i32
@@ -338,13 +339,29 @@ def sign_selection_errors(keys: torch.Tensor, q: torch.Tensor, candidate_bits, b
     return errors
 
 
+def sign_selection_choose(errors):
+    """The library's choice rule on error sums [C, S, 2] (host array or
+    tensor): returns (index, objective per candidate as a numpy array)."""
+    if isinstance(errors, torch.Tensor):
+        errors = errors.detach().cpu().numpy()
+    e = np.ascontiguousarray(errors, dtype=np.float64)
+    if e.ndim != 3 or e.shape[-1] != 2:
+        raise ValueError("errors must have shape [C, S, 2]")
+    C, S = e.shape[0], e.shape[1]
+    objective = np.empty(max(C, 1), dtype=np.float64)
+    index = ctypes.c_int(-1)
+    dp = ctypes.POINTER(ctypes.c_double)
+    _check(lib.axr_sign_selection_choose(e.ctypes.data_as(dp), C, S, ctypes.byref(index),
+                                         objective.ctypes.data_as(dp)))
+    return int(index.value), objective[:C]
+
+
 def select_sign_pattern(keys: torch.Tensor, q: torch.Tensor, candidate_bits, b: int):
-    """The candidate whose worst calibration sample has the smallest relative
-    score error sqrt(err / ref); returns (index, objective per candidate as a
-    numpy array).  Synchronises with the device to read the errors."""
-    e = sign_selection_errors(keys, q, candidate_bits, b).cpu().numpy()
-    objective = np.sqrt(e[..., 0] / e[..., 1]).max(axis=1)
-    return int(np.argmin(objective)), objective
+    """Error sums of every candidate on the GPU, then the library's choice
+    rule (the smallest worst-sample sqrt(err / ref)); returns (index,
+    objective per candidate).  Synchronises with the device to read the
+    sums."""
+    return sign_selection_choose(sign_selection_errors(keys, q, candidate_bits, b))
 
 
 def _quats(quats: torch.Tensor, d: int, device) -> torch.Tensor:

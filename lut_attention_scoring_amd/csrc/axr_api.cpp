@@ -436,6 +436,36 @@ int axr_sign_selection_errors(const void* keys, int dtype, const void* q, int q_
   return ok();
 }
 
+int axr_sign_selection_choose(const double* errors, int C, int S, int* index,
+                              double* objective) {
+  if (C < 1 || S < 1) return fail(AXR_EINVAL, "C=%d and S=%d must be positive", C, S);
+  if (errors == nullptr || index == nullptr)
+    return fail(AXR_EINVAL, "errors and index must be non-null");
+  const int64_t n = static_cast<int64_t>(C) * S * 2;
+  for (int64_t i = 0; i < n; ++i) {
+    if (!(errors[i] >= 0.0))
+      return fail(AXR_EINVAL, "error sum %lld is negative or NaN", static_cast<long long>(i));
+  }
+  int best = 0;
+  double best_obj = 0.0;
+  for (int c = 0; c < C; ++c) {
+    double worst = 0.0;
+    for (int i = 0; i < S; ++i) {
+      const double err = errors[(static_cast<int64_t>(c) * S + i) * 2];
+      const double ref = errors[(static_cast<int64_t>(c) * S + i) * 2 + 1];
+      const double r = ref > 0.0 ? std::sqrt(err / ref) : (err > 0.0 ? HUGE_VAL : 0.0);
+      worst = std::max(worst, r);
+    }
+    if (objective != nullptr) objective[c] = worst;
+    if (c == 0 || worst < best_obj) {
+      best = c;
+      best_obj = worst;
+    }
+  }
+  *index = best;
+  return ok();
+}
+
 int axr_decode_step(const void* q, int q_dtype, const void* k_new, int k_dtype,
                     const uint32_t* sign_bits, const int32_t* pos, int B, int Hq, int Hkv,
                     int64_t T, int64_t t_cap, int d, int b, uint32_t* packed, float* norms,

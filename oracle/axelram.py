@@ -421,9 +421,22 @@ def sign_selection_errors(keys, q, candidate_bits, b: int) -> np.ndarray:
 
 def select_sign_pattern(errors):
     """The candidate whose worst calibration sample has the smallest relative
-    score error sqrt(err / ref); returns (index, objective per candidate)."""
+    score error sqrt(err / ref); returns (index, objective per candidate).
+    The first candidate wins a tie.  A sample whose exact scores are all zero
+    (ref = 0, e.g. a zero query) has no relative error to measure: it counts
+    0 when its table scores are zero too (err = 0) and +inf otherwise.
+    Negative or NaN sums are rejected."""
     e = np.asarray(errors, dtype=np.float64)
-    objective = np.sqrt(e[..., 0] / e[..., 1]).max(axis=1)
+    if e.ndim != 3 or e.shape[-1] != 2 or e.shape[0] < 1 or e.shape[1] < 1:
+        raise ValueError("errors must be [C >= 1][S >= 1][2]")
+    if not np.all(e >= 0.0):
+        raise ValueError("error sums must be nonnegative numbers")
+    err, ref = e[..., 0], e[..., 1]
+    ratio = np.full(err.shape, np.inf)
+    pos = ref > 0.0
+    ratio[pos] = err[pos] / ref[pos]
+    ratio[~pos & (err == 0.0)] = 0.0
+    objective = np.sqrt(ratio).max(axis=1)
     return int(np.argmin(objective)), objective
 
 

@@ -239,6 +239,45 @@ def test_sign_selection_validation():
     assert sel(C=0, keys=None, cand=None, errors=None, ws=None)[0] == axr.OK
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_sign_selection_choose_matches_oracle(seed):
+    """The library's choice rule (host) against the oracle's on random sums,
+    with zero-reference samples (error zero and nonzero) and exact ties."""
+    rng = np.random.default_rng(seed)
+    C, S = int(rng.integers(1, 40)), int(rng.integers(1, 9))
+    e = rng.uniform(0.0, 2.0, size=(C, S, 2)) ** 3
+    e[rng.random((C, S)) < 0.1, 1] = 0.0
+    e[rng.random((C, S)) < 0.1, 0] = 0.0
+    if C > 2:
+        e[C - 1] = e[C // 2]                       # a tie with an earlier candidate
+    idx, obj = axr.sign_selection_choose(e)
+    oidx, oobj = A.select_sign_pattern(e)
+    assert idx == oidx
+    assert np.array_equal(obj, oobj)
+
+
+def test_sign_selection_choose_validation():
+    f = axr.lib.axr_sign_selection_choose
+    e = np.ones((3, 2, 2))
+    dp = ctypes.POINTER(ctypes.c_double)
+    idx = ctypes.c_int(-7)
+
+    def ch(arr=e, C=3, S=2, index=ctypes.byref(idx)):
+        ptr = None if arr is None else np.ascontiguousarray(arr).ctypes.data_as(dp)
+        return _status(f, ptr, C, S, index, None)
+    assert ch()[0] == axr.OK and idx.value == 0
+    assert ch(C=0)[0] == axr.EINVAL
+    assert ch(S=0)[0] == axr.EINVAL
+    assert ch(arr=None)[0] == axr.EINVAL
+    assert ch(index=None)[0] == axr.EINVAL
+    for bad in (np.nan, -0.5):
+        e2 = e.copy()
+        e2[2, 1, 0] = bad
+        idx.value = -7
+        st, msg = ch(arr=e2)
+        assert st == axr.EINVAL and "negative or NaN" in msg and idx.value == -7
+
+
 def test_decode_step_validation():
     f = axr.lib.axr_decode_step
 

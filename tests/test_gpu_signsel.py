@@ -103,9 +103,13 @@ def test_selection_full_calibration_set():
     m = axr()
     cal = W.calibration_samples()
     cands = W.sign_candidates(128)
-    idx, objective = m.select_sign_pattern(cal["keys"].to(DEV), cal["q"].to(DEV), cands, 4)
+    keys, q = cal["keys"].to(DEV), cal["q"].to(DEV)
+    idx, objective = m.select_sign_pattern(keys, q, cands, 4)
     assert objective.shape == (len(cands),) and np.all(np.isfinite(objective))
-    assert idx == int(np.argmin(objective))
+    # the library's choice equals the oracle's rule applied to the GPU's sums
+    e = m.sign_selection_errors(keys, q, cands, 4).cpu().numpy()
+    oidx, oobj = A.select_sign_pattern(e)
+    assert idx == oidx and np.array_equal(objective, oobj)
     worst = int(np.argmax(objective))
     _check(cal["keys"], cal["q"], cands, 4, sorted({0, idx, worst}), "full")
 
@@ -131,4 +135,23 @@ def test_selection_errors_random_shapes(i):
         rng.standard_normal(d)) + 0.3).astype(np.float32)).to(dtype)
     q = torch.from_numpy(rng.standard_normal((S, B, Hkv * G, d)).astype(np.float32)).to(dtype)
     cands = rng.integers(0, 2, size=(C, d)).astype(np.uint8)
-    _check(keys, q, cands, b, range(C), label)
+    e = _check(keys, q, cands, b, range(C), label)
+    idx, obj = axr().sign_selection_choose(e)
+    oidx, oobj = A.select_sign_pattern(e)
+    assert idx == oidx and np.array_equal(obj, oobj), label
+
+
+def test_selection_with_a_zero_query_sample():
+    """A calibration sample whose queries are all zero has no exact score
+    mass (ref = 0) and zero table scores (err = 0): it counts 0 and the
+    choice is made by the other samples, as the oracle's rule says."""
+    m = axr()
+    cal = W.calibration_samples(count=3, T=256, seed=301)
+    q = cal["q"].clone()
+    q[1] = 0
+    cands = W.sign_candidates(128, count=6)
+    e = m.sign_selection_errors(cal["keys"].to(DEV), q.to(DEV), cands, 3).cpu().numpy()
+    assert np.all(e[:, 1, :] == 0.0)
+    idx, obj = m.sign_selection_choose(e)
+    oidx, oobj = A.select_sign_pattern(e)
+    assert idx == oidx and np.array_equal(obj, oobj) and np.all(np.isfinite(obj))

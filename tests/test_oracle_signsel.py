@@ -80,6 +80,25 @@ def test_selection_takes_the_best_worst_case():
     np.testing.assert_allclose(obj, [2.0, 1.5, 3.0])
 
 
+def test_selection_zero_reference_and_ties():
+    """A sample with no exact score mass counts 0 if its table scores are zero
+    too and +inf otherwise; equal objectives go to the first candidate."""
+    err = np.array([[[0.0, 0.0], [1.0, 4.0]],       # worst max(0, 0.5) = 0.5
+                    [[1e-30, 0.0], [0.0, 1.0]],     # inf
+                    [[0.25, 1.0], [0.0, 9.0]]])     # worst 0.5: ties with 0
+    idx, obj = A.select_sign_pattern(err)
+    assert idx == 0
+    assert obj[0] == 0.5 and obj[1] == np.inf and obj[2] == 0.5
+
+
+@pytest.mark.parametrize("bad", [np.nan, -1.0])
+def test_selection_rejects_bad_sums(bad):
+    err = np.ones((2, 2, 2))
+    err[1, 0, 1] = bad
+    with pytest.raises(ValueError):
+        A.select_sign_pattern(err)
+
+
 def test_calibration_generator_shapes_and_candidates():
     cal = W.calibration_samples(count=3, T=16)
     assert tuple(cal["keys"].shape) == (3, 1, 2, 16, 128)
