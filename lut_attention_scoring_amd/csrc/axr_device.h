@@ -32,6 +32,16 @@ __device__ __forceinline__ float lane_xor(float v) {
   return __uint_as_float(lane_xor_u32<M>(__float_as_uint(v)));
 }
 
+// a * b rounded to fp32 on its own: never fused into a later add, so that
+// the softmax partials and the row normalisation see the same scaled score
+// (with a fused multiply-add in one place and a rounded product in the
+// other, the row maximum's own exponent would differ from 0 by the product's
+// rounding, which reaches whole units once |a * b| passes ~1e7).
+__device__ __forceinline__ float mul_rounded(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+
 // Right rotation of an N-word little-endian bit string by r bits, 0 <= r < 32.
 template <int N>
 __device__ __forceinline__ void rotate_right(uint32_t (&w)[N], uint32_t r) {

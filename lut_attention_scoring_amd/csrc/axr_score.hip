@@ -648,7 +648,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
               __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), rsc,
                                                     vsc[t4], tb_rel * 4u, 0);
             }
-            if (want_lse && valid) lse_push(sm_m[t4], sm_l[t4], sv * lse_scale);
+            if (want_lse && valid) lse_push(sm_m[t4], sm_l[t4], mul_rounded(sv, lse_scale));
           }
         } else {
           // sum over the LPK lanes of the key (exact integer sums)
@@ -666,7 +666,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
                 const float sc = static_cast<float>(static_cast<int32_t>(acc[il][g])) * ginv[g];
                 const float sv = (nk[il] * sc) * ginv2[g];
                 scores[(static_cast<size_t>(bi) * prm.Hq + h0 + g) * prm.T + t] = sv;
-                if (want_lse) lse_push(sm_m[0], sm_l[0], sv * lse_scale);
+                if (want_lse) lse_push(sm_m[0], sm_l[0], mul_rounded(sv, lse_scale));
               }
             }
           }

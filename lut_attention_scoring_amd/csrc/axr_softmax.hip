@@ -88,7 +88,8 @@ __global__ __launch_bounds__(kThreads) void softmax_rows(float* __restrict__ sco
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k) {
     const int64_t t = t0 + static_cast<int64_t>(k) * kThreads + threadIdx.x;
-    if (t < t1) r[t] = expf(fmaf(scale, v[k], -m)) * inv_l;
+    // the scaled score rounded as the score kernel rounded it for (m, l)
+    if (t < t1) r[t] = expf(mul_rounded(scale, v[k]) - m) * inv_l;
   }
 }
 
