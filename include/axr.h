@@ -205,6 +205,25 @@ int axr_score_softmax(const void* q, int q_dtype, const uint32_t* packed, const 
                       float* lse, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * axr_score_softmax without a workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The split-T partials go to a device array that the
+ * library holds, 1 MiB per device, allocated with the library's code object
+ * and kept until the process ends; this call allocates nothing.  Every call
+ * on a device uses that device's array: calls that overlap on one device
+ * (other streams, other threads) race on it and must be serialised by the
+ * caller.  The array needs no clearing (every partial the second kernel
+ * reads is written by the first).  Sizes whose partials
+ * (B * Hq * tiles * 8 bytes, as axr_score_softmax_workspace reports) exceed
+ * 1 MiB are rejected with AXR_EUNSUPPORTED before any device work.  Otherwise
+ * arguments, results and errors are those of axr_score_softmax.
+ */
+int axr_score_softmax_noalloc(const void* q, int q_dtype, const uint32_t* packed,
+                              const float* norms, const uint32_t* sign_bits, int B, int Hq,
+                              int Hkv, const int32_t* lens, int64_t T, int64_t t_cap, int d,
+                              int b, float scale, float* probs, float* lse, void* stream);
+
+/*
  * One-time sign-pattern selection (AXELRAM, Abstract: gradient-free, a few
  * hundred candidate sign patterns, a few calibration samples, chosen once).
  * The pages rank candidates by perplexity, which needs model weights; this

@@ -20,6 +20,7 @@ import torch
 __all__ = [
     "AxrError", "LIB_PATH", "lib", "version", "codebook", "sign_words",
     "packed_words", "quantize_keys", "append_keys", "decode_step", "score", "score_softmax",
+    "score_softmax_noalloc",
     "transform", "sign_selection_errors", "sign_selection_choose", "select_sign_pattern",
     "quantize_keys_isoquant", "transform_isoquant",
     "probe_read_stream",
@@ -73,6 +74,9 @@ def _load():
     so.axr_score_softmax.restype = i32
     so.axr_score_softmax.argtypes = [vp, i32, vp, vp, u32p, i32, i32, i32, vp, i64, i64, i32,
                                      i32, ctypes.c_float, vp, vp, vp, i64, vp]
+    so.axr_score_softmax_noalloc.restype = i32
+    so.axr_score_softmax_noalloc.argtypes = [vp, i32, vp, vp, u32p, i32, i32, i32, vp, i64, i64,
+                                             i32, i32, ctypes.c_float, vp, vp, vp]
     so.axr_sign_selection_workspace.restype = i32
     so.axr_sign_selection_workspace.argtypes = [i32, i32, i32, i32, i64, i32, i32,
                                                 ctypes.POINTER(ctypes.c_int64)]
@@ -310,6 +314,36 @@ def score_softmax(q: torch.Tensor, packed: torch.Tensor, norms: torch.Tensor, si
                                  None if lens is None else lens.data_ptr(), T, t_cap, d, b,
                                  scale, out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(), _stream(q)))
+    return out, lse
+
+
+def score_softmax_noalloc(q: torch.Tensor, packed: torch.Tensor, norms: torch.Tensor,
+                          sign_bits, b: int, out: torch.Tensor, lse: torch.Tensor,
+                          scale: float = None, T: int = None, lens: torch.Tensor = None):
+    """score_softmax with the split-T partials in the library's own device
+    array (no allocation here or in the library): out [B, Hq, T] and lse
+    [B, Hq] must be given.  Calls that overlap on one device race on that
+    array."""
+    B, Hq, d = q.shape
+    Bk, Hkv, t_cap, W = packed.shape
+    if Bk != B or W != packed_words(d, b) or tuple(norms.shape) != (B, Hkv, t_cap):
+        raise ValueError("q, packed and norms shapes disagree")
+    T = t_cap if T is None else int(T)
+    scale = 1.0 / float(d) ** 0.5 if scale is None else float(scale)
+    _need_dtype(packed, torch.int32, "packed")
+    _need_dtype(norms, torch.float32, "norms")
+    _need_out(out, (B, Hq, T), torch.float32, "out")
+    _need_out(lse, (B, Hq), torch.float32, "lse")
+    _need_cuda(q, packed, norms, out, lse)
+    if lens is not None:
+        if lens.dtype != torch.int32 or tuple(lens.shape) != (B,):
+            raise ValueError("lens must be an int32 tensor of shape [B]")
+        _need_cuda(lens)
+    words, wp = _words_ptr(sign_words(sign_bits))
+    _check(lib.axr_score_softmax_noalloc(q.data_ptr(), _dtype_code(q), packed.data_ptr(),
+                                         norms.data_ptr(), wp, B, Hq, Hkv,
+                                         None if lens is None else lens.data_ptr(), T, t_cap, d,
+                                         b, scale, out.data_ptr(), lse.data_ptr(), _stream(q)))
     return out, lse
 
 

@@ -314,30 +314,43 @@ int axr_score_softmax_workspace(int B, int Hq, int Hkv, int64_t T, int d, int b,
   return ok();
 }
 
-int axr_score_softmax(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
-                      const uint32_t* sign_bits, int B, int Hq, int Hkv, const int32_t* lens,
-                      int64_t T, int64_t t_cap, int d, int b, float scale, float* probs,
-                      float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
+// axr_score_softmax, with the split-T partials either in the caller's
+// workspace or (use_scratch) in the library's own device array.
+static int score_softmax_common(const void* q, int q_dtype, const uint32_t* packed,
+                                const float* norms, const uint32_t* sign_bits, int B, int Hq,
+                                int Hkv, const int32_t* lens, int64_t T, int64_t t_cap, int d,
+                                int b, float scale, float* probs, float* lse, void* workspace,
+                                int64_t workspace_bytes, bool use_scratch, void* stream) {
   int rc = check_score_sizes(d, b, q_dtype, sign_bits, B, Hq, Hkv, T, t_cap);
   if (rc != AXR_OK) return rc;
   if (!std::isfinite(scale)) return fail(AXR_EINVAL, "scale must be finite");
   if (B == 0 || T == 0) return ok();
   if (q == nullptr || packed == nullptr || norms == nullptr || probs == nullptr)
     return fail(AXR_EINVAL, "q, packed, norms and probs must be non-null");
-  if (workspace == nullptr) return fail(AXR_EINVAL, "workspace is null");
+  if (!use_scratch && workspace == nullptr) return fail(AXR_EINVAL, "workspace is null");
   if (!aligned(q, 16)) return fail(AXR_EALIGN, "q must be 16-byte aligned");
   if (!aligned(packed, 16)) return fail(AXR_EALIGN, "packed must be 16-byte aligned");
   if (!aligned(norms, 4) || !aligned(probs, 4) || (lse != nullptr && !aligned(lse, 4)) ||
       (lens != nullptr && !aligned(lens, 4)))
     return fail(AXR_EALIGN, "norms, probs, lse and lens must be 4-byte aligned");
-  if (!aligned(workspace, 8)) return fail(AXR_EALIGN, "workspace must be 8-byte aligned");
+  if (!use_scratch && !aligned(workspace, 8))
+    return fail(AXR_EALIGN, "workspace must be 8-byte aligned");
   axr::ScoreParams plan;
   if (score_tiles(sign_bits, B, Hq, Hkv, T, t_cap, d, b, &plan) != 0)
     return fail(AXR_EUNSUPPORTED, "no launch configuration for these sizes");
   const int64_t need = static_cast<int64_t>(B) * Hq * plan.tiles * 2 * 4;
-  if (workspace_bytes < need)
+  if (use_scratch) {
+    if (need > axr::kScratchBytes)
+      return fail(AXR_EUNSUPPORTED,
+                  "these sizes need %lld bytes of split-T partials, more than the %lld bytes "
+                  "of library scratch (use axr_score_softmax with a workspace)",
+                  static_cast<long long>(need), static_cast<long long>(axr::kScratchBytes));
+    const int err = axr::scratch_address(&workspace);
+    if (err != 0) return hip_status(err, "library scratch address");
+  } else if (workspace_bytes < need) {
     return fail(AXR_EINVAL, "workspace of %lld bytes is smaller than the %lld required",
                 static_cast<long long>(workspace_bytes), static_cast<long long>(need));
+  }
   axr::ScoreParams p = score_params(sign_bits, Hq, Hkv, T, t_cap, d, b, lens);
   p.partials = static_cast<float*>(workspace);
   p.scale = scale;
@@ -346,6 +359,22 @@ int axr_score_softmax(const void* q, int q_dtype, const uint32_t* packed, const 
   err = axr::launch_softmax(probs, p.partials, lens, B, Hq, T, plan.tiles, plan.tile_len, scale,
                             lse, stream);
   return hip_status(err, "softmax kernel launch");
+}
+
+int axr_score_softmax(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
+                      const uint32_t* sign_bits, int B, int Hq, int Hkv, const int32_t* lens,
+                      int64_t T, int64_t t_cap, int d, int b, float scale, float* probs,
+                      float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
+  return score_softmax_common(q, q_dtype, packed, norms, sign_bits, B, Hq, Hkv, lens, T, t_cap,
+                              d, b, scale, probs, lse, workspace, workspace_bytes, false, stream);
+}
+
+int axr_score_softmax_noalloc(const void* q, int q_dtype, const uint32_t* packed,
+                              const float* norms, const uint32_t* sign_bits, int B, int Hq,
+                              int Hkv, const int32_t* lens, int64_t T, int64_t t_cap, int d,
+                              int b, float scale, float* probs, float* lse, void* stream) {
+  return score_softmax_common(q, q_dtype, packed, norms, sign_bits, B, Hq, Hkv, lens, T, t_cap,
+                              d, b, scale, probs, lse, nullptr, 0, true, stream);
 }
 
 // Workspace layout of the sign-pattern selection (offsets 256-byte aligned):

@@ -76,6 +76,12 @@ struct ScoreParams {
   float tpos[kMaxLevels / 2];     // positive thresholds times sqrt(d)
 };
 
+// Library-held device scratch of axr_score_softmax_noalloc (split-T
+// partials), one array per device, and its device address on the current
+// device (looked up once per device; returns a hipError_t value as int).
+constexpr int64_t kScratchBytes = 1 << 20;
+int scratch_address(void** ptr);
+
 // Launchers (return a hipError_t value as int; 0 = success).
 int launch_write(const void* keys, int dtype, int64_t n, int d, int b, const WriteParams& p,
                  uint32_t* packed, float* norms, float* y, int mode, void* stream,

@@ -216,6 +216,27 @@ def test_softmax_validation():
     assert sm(lse=FAKE + 2)[0] == axr.EALIGN
 
 
+def test_softmax_noalloc_validation():
+    """The entry point without a workspace checks everything the workspace one
+    does, and rejects sizes whose partials exceed its 1 MiB of library scratch
+    before any device work (pointers here are never dereferenced)."""
+    g = axr.lib.axr_score_softmax_noalloc
+
+    def na(B=2, Hq=8, Hkv=2, T=64, q=FAKE, scale=0.1, probs=FAKE, lse=None):
+        return _status(g, q, axr.F16, FAKE, FAKE, SIGNS, B, Hq, Hkv, None, T, T, 128, 3,
+                       ctypes.c_float(scale), probs, lse, None)
+    assert na(scale=float("nan"))[0] == axr.EINVAL
+    assert na(q=None)[0] == axr.EINVAL
+    assert na(probs=FAKE + 2)[0] == axr.EALIGN
+    assert na(B=0, q=None, probs=None)[0] == axr.OK
+    # 4096 x 64 rows x 1 tile x 8 B = 2 MiB of partials
+    st, msg = na(B=4096, Hq=64, Hkv=1, T=1)
+    assert st == axr.EUNSUPPORTED and "1048576 bytes of library scratch" in msg
+    n = ctypes.c_int64(-1)
+    assert _status(axr.lib.axr_score_softmax_workspace, 4096, 64, 1, 1, 128, 3,
+                   ctypes.byref(n))[0] == axr.OK and n.value > 1 << 20
+
+
 def test_sign_selection_validation():
     n = ctypes.c_int64(-1)
     f = axr.lib.axr_sign_selection_workspace
