@@ -7,20 +7,35 @@ Lloyd-Max bucketize, pack) and score every query head against the packed
 cache (query transform, LUT in LDS, lookup-accumulate).  Inputs are resident
 in HBM before timing starts.
 
-Prints one JSON line.  Per-kernel durations come from HIP events recorded on
-the stream the kernels run on; the score kernel is also timed alone on a cold
-cache (2 GiB of reads between launches) for its HBM roofline.
+Prints one JSON line:
+  * value: keys per second through the timed steps (whole-job throughput);
+  * roofline: the score kernel (the kernel the bandwidth target names) with
+    every launch reading its records from HBM (back to back over four copies
+    of the cache, more than twice the Infinity Cache), duration from HIP
+    events on the stream it runs on; roofline_write: the write kernel alike;
+  * configs: write and score kernel times on every workload shape (tiny;
+    LLaMA decode; all 36 Qwen2.5-3B layers; long context at b = 2, 3, 4; the
+    nine write-sweep cells), each kernel cycling over enough buffer copies
+    that its inputs come from HBM;
+  * cpu_baseline: the fp64 oracle on bounded samples of every workload, its
+    quantize and score rates reported separately.
 
-With --workloads it instead prints one JSON line per workload shape with the
-write and score kernel times (--steps launches each after --warmup).
+--profile KERNEL runs only that kernel's timed loop (for a rocprofv3 kernel
+trace or counter pass whose averages then cover exactly those launches) and
+prints its HIP-event figure.
 """
 
 import argparse
 import gc
+import glob
+import hashlib
 import json
+import math
 import os
+import re
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -29,33 +44,45 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "quantized keys scored/sec + achieved HBM GB/s (d=128, b=3, GQA decode)"
 CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
-# HBM bytes per launch on this workload from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE passes (profiles/*_llama31_8b_decode_d128_b3.md): FETCH_SIZE x 2.0
-# + WRITE_SIZE x 1.0, factors from a 2 GiB read and a 2 GiB fill in the same
-# runs.  Valid only for the kernel sources they were taken on (SHA-1 of the
-# files below); otherwise traffic is reported as null.
-COUNTER_TRAFFIC = {
-    "write": {"sources": ["axr_write.hip", "axr_keyquant.h", "axr_device.h", "axr_internal.h"],
-              "sha1": "fb9d2b6f897ea1fac17492de7689ee757b947702",
-              "bytes": (262196.1 * 2.0 + 106531.1) * 1024},
-    "score": {"sources": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
-              "sha1": "fee22021ac8518faff9cdd4adecb29aa7743c683",
-              "bytes": (53432.2 * 2.0 + 34485.5) * 1024},
+# Sources whose compiled code a kernel's counter figures depend on.
+KERNEL_SOURCES = {
+    "write": ["axr_write.hip", "axr_keyquant.h", "axr_device.h", "axr_internal.h"],
+    "score": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
 }
+
+WARM_MS = 30.0   # time each kernel runs untimed before its timed launches
+SETTLE_MS = 100.0  # step loop run untimed before the warmup steps
+
+
+def sources_sha1(kernel):
+    h = hashlib.sha1()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def counter_traffic(kernel):
-    import hashlib
-    entry = COUNTER_TRAFFIC[kernel]
-    h = hashlib.sha1()
-    for name in entry["sources"]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
-    return entry["bytes"] if h.hexdigest() == entry["sha1"] else None
-
-
-WARM_MS = 30.0   # time each kernel runs untimed before its timed launches
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+    summarised in profiles/: each summary carries a line
+      counter-traffic: kernel=K sources_sha1=S fetch_kib=F write_kib=W
+                       fetch_factor=a write_factor=b
+    written from the run that took the counters (S is the SHA-1 of the
+    kernel's sources in that run).  Bytes = (F a + W b) * 1024 if S equals the
+    current sources' SHA-1, else None (the kernel changed since)."""
+    want = sources_sha1(kernel)
+    pat = re.compile(r"counter-traffic:\s*kernel=(\w+)\s+sources_sha1=([0-9a-f]+)\s+"
+                     r"fetch_kib=([0-9.]+)\s+write_kib=([0-9.]+)\s+fetch_factor=([0-9.]+)\s+"
+                     r"write_factor=([0-9.]+)")
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        with open(path) as f:
+            for m in pat.finditer(f.read()):
+                if m.group(1) == kernel and m.group(2) == want:
+                    fk, wk, ff, wf = (float(m.group(i)) for i in range(3, 7))
+                    return (fk * ff + wk * wf) * 1024.0
+    return None
 
 
 def launches_ms(torch, stream, fn, reps, warm_ms=WARM_MS):
@@ -63,11 +90,9 @@ def launches_ms(torch, stream, fn, reps, warm_ms=WARM_MS):
     recorded on the stream the kernels run on.  Before the start event the
     kernel runs untimed for `warm_ms` of wall time, and a few more launches
     are queued right before the event: the chip needs several milliseconds of
-    a given load before its clock settles (the first couple of hundred score
-    launches after other work run up to a third slower), and that transient
-    belongs to neither kernel.  Python's cyclic garbage collector is held
-    off (a full collection of this process stalls the launching thread for
-    tens of milliseconds)."""
+    a given load before its clock settles, and that transient belongs to no
+    kernel.  Python's cyclic garbage collector is held off (a full collection
+    of this process stalls the launching thread for tens of milliseconds)."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     gc.collect()
     gc.disable()
@@ -89,6 +114,24 @@ def launches_ms(torch, stream, fn, reps, warm_ms=WARM_MS):
     return e0.elapsed_time(e1) / reps
 
 
+class Rotor:
+    """Calls fn(copy) cycling over buffer copies."""
+
+    def __init__(self, copies, fn):
+        self.copies, self.fn, self.i = copies, fn, 0
+
+    def __call__(self):
+        c = self.copies[self.i % len(self.copies)]
+        self.i += 1
+        self.fn(c)
+
+
+def n_copies(bytes_per_copy, min_copies=4, cycle_bytes=1 << 30):
+    """Copies to cycle over so that one cycle moves >= 1 GiB (four times the
+    256 MB Infinity Cache) and at least `min_copies`."""
+    return max(min_copies, math.ceil(cycle_bytes / max(bytes_per_copy, 1)))
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -97,154 +140,372 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # ~17 ms of steps: the clock takes ~10 ms of this load to settle
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed step loop before the warmup steps (clock settling)")
     ap.add_argument("--cold-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workloads", action="store_true",
-                    help="instead of the benchmark line: time the write and score kernels "
-                         "on every workload shape, one JSON line per workload")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the every-workload section")
+    ap.add_argument("--profile", choices=["score_rotating", "score_resident", "write",
+                                          "qwen_score", "long_score_b4"],
+                    help="run only this kernel's timed loop and print its figure")
     return ap.parse_args()
 
 
-def workload_table(args):
-    """Write and score kernel times on every workload shape: each kernel is
-    launched `steps` times back to back between HIP events on its stream,
-    right behind untimed launches of the same kernel (inputs resident in
-    HBM, Python's collector off)."""
-    import torch
-    import lut_attention_scoring_amd as axr
-    import workloads as W
+# ---------------------------------------------------------------------------
+# Inputs
+# ---------------------------------------------------------------------------
 
+def gen_parallel(fns, workers=16):
+    """Runs the generators in threads (numpy's generators release the GIL)."""
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(lambda f: f(), fns))
+
+
+def score_bytes_per_key(d, b, G):
+    return d * b // 8 + 4 + 4 * G
+
+
+def write_bytes_per_key(d, b, elt):
+    return d * elt + d * b // 8 + 4
+
+
+# ---------------------------------------------------------------------------
+# Every workload shape
+# ---------------------------------------------------------------------------
+
+def time_write(torch, axr, stream, keys, bits, b, reps):
+    """Write kernel over rotating copies of the keys (records and norms of
+    each copy written to their own buffers)."""
+    dev = keys.device
+    n = keys.numel() // keys.shape[-1]
+    d = keys.shape[-1]
+    per = write_bytes_per_key(d, b, keys.element_size()) * n
+    k = n_copies(per, min_copies=2)
+    copies = [keys] + [keys.clone() for _ in range(k - 1)]
+    outs = [(torch.empty(n, d * b // 32, dtype=torch.int32, device=dev),
+             torch.empty(n, dtype=torch.float32, device=dev)) for _ in range(k)]
+    pairs = list(zip(copies, outs))
+    rot = Rotor(pairs, lambda c: axr.quantize_keys(c[0], bits, b, packed=c[1][0],
+                                                   norms=c[1][1]))
+    ms = launches_ms(torch, stream, rot, max(reps, k) // k * k)
+    del copies, outs, pairs
+    return {"us": ms * 1e3, "keys_per_s": n / (ms * 1e-3), "bytes": per,
+            "GB_per_s": per / (ms * 1e6), "frac_hbm": per / (ms * 1e6) / HBM_PEAK_GBS,
+            "copies": k}
+
+
+def time_score(torch, axr, stream, q, packed, norms, bits, b, reps, min_copies=4):
+    """Score kernel over rotating copies of records, norms and score rows."""
+    B, Hq, _ = q.shape
+    _, Hkv, T, W = packed.shape
+    n = B * Hkv * T
+    d = q.shape[-1]
+    per = score_bytes_per_key(d, b, Hq // Hkv) * n
+    k = n_copies(per, min_copies=min_copies)
+    copies = [(packed, norms, torch.empty(B, Hq, T, device=q.device))] + [
+        (packed.clone(), norms.clone(), torch.empty(B, Hq, T, device=q.device))
+        for _ in range(k - 1)]
+    rot = Rotor(copies, lambda c: axr.score(q, c[0], c[1], bits, b, out=c[2]))
+    ms = launches_ms(torch, stream, rot, max(reps, k) // k * k)
+    del copies
+    return {"us": ms * 1e3, "keys_per_s": n / (ms * 1e-3),
+            "head_scores_per_s": n * (Hq // Hkv) / (ms * 1e-3), "bytes": per,
+            "GB_per_s": per / (ms * 1e6), "frac_hbm": per / (ms * 1e6) / HBM_PEAK_GBS,
+            "copies": k}
+
+
+def configs_section(torch, axr, W, stream, reps):
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
+    out = {}
 
-    def per_launch_ms(fn):
-        return launches_ms(torch, stream, fn, args.steps)
+    # tiny: 4096 keys, one query (latency-bound; fits every cache)
+    w = W.tiny()
+    keys, q = w["keys"].to(dev), w["q"].to(dev)
+    packed, norms = axr.quantize_keys(keys, w["sign_bits"], 3)
+    wr = launches_ms(torch, stream, lambda: axr.quantize_keys(keys, w["sign_bits"], 3,
+                                                              packed=packed, norms=norms), reps)
+    sc = torch.empty(1, 1, 4096, device=dev)
+    sr = launches_ms(torch, stream, lambda: axr.score(q, packed.view(1, 1, 4096, 12),
+                                                      norms.view(1, 1, 4096), w["sign_bits"], 3,
+                                                      out=sc), reps)
+    out["tiny_d128_b3_n4096"] = {"keys": 4096, "write_us": wr * 1e3, "score_us": sr * 1e3,
+                                 "note": "back to back; 0.2 MiB per launch, latency-bound"}
+    log("configs: tiny done")
 
-    cases = [("tiny_d128_b3", lambda: W.tiny()),
-             ("llama31_8b_decode_d128_b3", lambda: W.llama_decode()),
-             ("qwen25_3b_layer0_d128_b4", lambda: W.qwen_layer(0)),
-             ("qwen25_3b_layer35_d128_b4", lambda: W.qwen_layer(W.QWEN_LAYERS - 1))]
-    cases += [(f"long_context_d128_b{b}", lambda b=b: W.long_context(b=b)) for b in (2, 3, 4)]
-    cases += [(f"write_sweep_d{d}_b{b}", lambda d=d, b=b: W.write_sweep(d=d, b=b))
-              for d in (128, 256, 512) for b in (2, 3, 4)]
-    for name, make in cases:
-        w = make()
-        keys = w["keys"].to(dev)
-        B, Hkv, T, d = keys.shape
-        b, bits = w["b"], w["sign_bits"]
-        n = B * Hkv * T
+    # LLaMA-3.1-8B decode cache (the headline workload)
+    w = W.llama_decode()
+    keys, q, bits = w["keys"].to(dev), w["q"].to(dev), w["sign_bits"]
+    del w
+    packed, norms = axr.quantize_keys(keys, bits, 3)
+    out["llama31_8b_gqa_decode_d128_b3"] = {
+        "keys": keys.numel() // 128,
+        "write": time_write(torch, axr, stream, keys, bits, 3, reps),
+        "score": time_score(torch, axr, stream, q, packed, norms, bits, 3, reps)}
+    del keys, q, packed, norms
+    torch.cuda.empty_cache()
+    log("configs: LLaMA done")
+
+    # Qwen2.5-3B: all 36 layers, each with its own cache; one pass quantizes
+    # (then scores) every layer back to back, 36 x 186 MB from HBM
+    layers = gen_parallel([lambda l=l: W.qwen_layer(l) for l in range(W.QWEN_LAYERS)])
+    L = len(layers)
+    bits = layers[0]["sign_bits"]
+    lk = [x["keys"].to(dev) for x in layers]
+    lq = [x["q"].to(dev) for x in layers]
+    del layers
+    lp = [axr.quantize_keys(k, bits, 4) for k in lk]
+    B, Hkv, T, d = lk[0].shape
+    Hq = lq[0].shape[1]
+    ls = [torch.empty(B, Hq, T, device=dev) for _ in range(L)]
+    n = B * Hkv * T
+
+    def write_all():
+        for k, (p, nm) in zip(lk, lp):
+            axr.quantize_keys(k, bits, 4, packed=p, norms=nm)
+
+    def score_all():
+        for qq, (p, nm), s in zip(lq, lp, ls):
+            axr.score(qq, p, nm, bits, 4, out=s)
+
+    passes = max(2, reps // 4)
+    wms = launches_ms(torch, stream, write_all, passes)
+    sms = launches_ms(torch, stream, score_all, passes)
+    wb = write_bytes_per_key(d, 4, 2) * n
+    sb = score_bytes_per_key(d, 4, Hq // Hkv) * n
+    out["qwen25_3b_layer_sweep_d128_b4"] = {
+        "layers": L, "keys_per_layer": n,
+        "write_all_layers_us": wms * 1e3, "score_all_layers_us": sms * 1e3,
+        "write_per_layer_us": wms * 1e3 / L, "score_per_layer_us": sms * 1e3 / L,
+        "write_GB_per_s": wb * L / (wms * 1e6), "score_GB_per_s": sb * L / (sms * 1e6),
+        "write_frac_hbm": wb * L / (wms * 1e6) / HBM_PEAK_GBS,
+        "score_frac_hbm": sb * L / (sms * 1e6) / HBM_PEAK_GBS,
+        "score_keys_per_s": n * L / (sms * 1e-3), "write_keys_per_s": n * L / (wms * 1e-3),
+        "note": "one pass = every layer back to back on its own cache (layer sum); "
+                f"{passes} passes timed"}
+    del lk, lq, lp, ls
+    torch.cuda.empty_cache()
+    log("configs: Qwen done")
+
+    # long context, b = 2, 3, 4 (the keys do not depend on b)
+    w = W.long_context(b=3)
+    keys, q, bits = w["keys"].to(dev), w["q"].to(dev), w["sign_bits"]
+    del w
+    lc = {}
+    for b in (2, 3, 4):
         packed, norms = axr.quantize_keys(keys, bits, b)
-        write_ms = per_launch_ms(lambda: axr.quantize_keys(keys, bits, b, packed=packed,
-                                                           norms=norms))
-        write_bytes = n * (d * keys.element_size() + d * b // 8 + 4)
-        line = {"workload": name, "keys": n, "d": d, "b": b, "key_dtype": str(keys.dtype),
-                "write_us": write_ms * 1e3, "write_GB_per_s": write_bytes / (write_ms * 1e6),
-                "write_frac_hbm": write_bytes / (write_ms * 1e6) / HBM_PEAK_GBS}
-        if w["q"] is not None:
-            q = w["q"].to(dev)
-            Hq = q.shape[1]
-            scores = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
-            score_ms = per_launch_ms(lambda: axr.score(q, packed, norms, bits, b, out=scores))
-            score_bytes = n * (d * b // 8 + 4 + 4 * (Hq // Hkv))
-            line.update({"G": Hq // Hkv, "score_us": score_ms * 1e3,
-                         "score_GB_per_s": score_bytes / (score_ms * 1e6),
-                         "score_frac_hbm": score_bytes / (score_ms * 1e6) / HBM_PEAK_GBS})
-            del q, scores
-        print(json.dumps(line), flush=True)
-        del keys, packed, norms, w
+        lc[f"b{b}"] = {"write": time_write(torch, axr, stream, keys, bits, b, reps),
+                       "score": time_score(torch, axr, stream, q, packed, norms, bits, b, reps)}
+        del packed, norms
+    out["long_context_t131072_d128"] = dict(keys=keys.numel() // 128, **lc)
+    del keys, q
+    torch.cuda.empty_cache()
+    log("configs: long context done")
+
+    # write sweep: 32768 tokens x 8 KV heads, d x b (the keys do not depend on b)
+    ws = {}
+    for d in (128, 256, 512):
+        w = W.write_sweep(d=d, b=3)
+        keys, bits = w["keys"].to(dev), w["sign_bits"]
+        del w
+        for b in (2, 3, 4):
+            ws[f"d{d}_b{b}"] = time_write(torch, axr, stream, keys, bits, b, reps)
+        del keys
         torch.cuda.empty_cache()
+    out["write_sweep_t32768x8"] = ws
+    log("configs: write sweep done")
+    return out
 
 
-def cpu_baseline(w):
-    """The fp64 oracle, as it stands, on batch elements [0, 6) of the same
-    workload (6 x 8 KV heads x 32768 tokens = 1572864 keys, 32 query heads)."""
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on bounded samples of every workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline():
+    """The fp64 oracle as it stands, on a bounded, stated sample of every
+    workload (quantize = write path, score = read path, timed separately).
+    BLAS threads are pinned to the process's CPU affinity count; only the
+    dense Hadamard product uses them, the rest of the oracle runs on one."""
     import numpy as np
     import threadpoolctl
+    import torch
+    import workloads as W
     from oracle import axelram as A
 
-    import torch
-    nb = 6
-    keys = w["keys"][0:nb].to(dtype=torch.float64).numpy()
-    q = w["q"][0:nb].to(dtype=torch.float64).numpy()
-    s = A.signs_from_bits(w["sign_bits"])
-    t0 = time.perf_counter()
-    wr = A.write_path(keys, s, w["b"])
-    A.read_path(q, wr["packed"], wr["norms"], s, w["b"])
-    dt = time.perf_counter() - t0
-    n = keys.shape[0] * keys.shape[1] * keys.shape[2]
-    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
-                   if p.get("user_api") == "blas"] or [1])
-    return {"value": n / dt, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"batch elements 0-{nb - 1} of 8: {n} keys ({nb} x 8 KV heads x 32768 tokens) "
-                      f"quantized and scored by 32 query heads each, fp64 numpy, {dt:.1f} s; "
-                      f"host reports {os.cpu_count()} CPUs"}
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    per = {}
 
+    def run(name, keys, q, bits, b, note):
+        k = keys.to(torch.float64).numpy()
+        s = A.signs_from_bits(bits)
+        t0 = time.perf_counter()
+        wr = A.write_path(k, s, b)
+        tq = time.perf_counter() - t0
+        n = int(np.prod(k.shape[:-1]))
+        entry = {"keys": n, "quantize_s": tq, "quantize_keys_per_s": n / tq, "sample": note}
+        if q is not None:
+            qq = q.to(torch.float64).numpy()
+            t0 = time.perf_counter()
+            A.read_path(qq, wr["packed"], wr["norms"], s, b)
+            ts = time.perf_counter() - t0
+            entry.update({"score_s": ts, "score_keys_per_s": n / ts,
+                          "quantize_and_score_keys_per_s": n / (tq + ts)})
+        per[name] = entry
+        return entry
+
+    with threadpoolctl.threadpool_limits(limits=cores, user_api="blas"):
+        w = W.tiny()
+        run("tiny_d128_b3_n4096", w["keys"], w["q"], w["sign_bits"], 3, "all 4096 keys, 1 query")
+        w = W.llama_decode(B=1, T=16384)
+        head = run("llama31_8b_gqa_decode_d128_b3", w["keys"], w["q"], w["sign_bits"], 3,
+                   "the workload's recipe at batch 1 and 16384 tokens: 8 KV heads x 16384 = "
+                   "131072 keys, 32 query heads")
+        del w
+        tq = ts = nk = 0.0
+        for layer in range(W.QWEN_LAYERS):
+            w = W.qwen_layer(layer, B=1, T=1024)
+            e = run(f"qwen_layer{layer}", w["keys"], w["q"], w["sign_bits"], 4, "")
+            tq, ts, nk = tq + e["quantize_s"], ts + e["score_s"], nk + e["keys"]
+            del per[f"qwen_layer{layer}"]
+        per["qwen25_3b_layer_sweep_d128_b4"] = {
+            "keys": int(nk), "quantize_keys_per_s": nk / tq, "score_keys_per_s": nk / ts,
+            "quantize_and_score_keys_per_s": nk / (tq + ts),
+            "quantize_s": tq, "score_s": ts,
+            "sample": "every one of the 36 layers, generated with batch 1 and 1024 tokens "
+                      "(2 KV heads, 16 query heads): 2048 keys per layer"}
+        w = W.long_context(b=3, T=8192)
+        for b in (2, 3, 4):
+            run(f"long_context_b{b}", w["keys"], w["q"], w["sign_bits"], b,
+                "the workload's recipe at 8192 tokens: 8 KV heads x 8192 = 65536 keys, "
+                "64 query heads")
+        del w
+        for d in (128, 256, 512):
+            w = W.write_sweep(d=d, b=3, T=4096)
+            for b in (2, 3, 4):
+                run(f"write_sweep_d{d}_b{b}", w["keys"], None, w["sign_bits"], b,
+                    "the workload's recipe at 4096 tokens: 8 KV heads x 4096 = 32768 keys "
+                    "(write path only)")
+            del w
+    total = sum(e.get("quantize_s", 0.0) + e.get("score_s", 0.0) for e in per.values())
+    return {"value": head["quantize_and_score_keys_per_s"], "unit": "keys/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": "LLaMA-3.1-8B decode cache recipe at batch 1, 8 KV heads x 16384 tokens "
+                      "(131072 keys) quantized and scored by 32 query heads, fp64 numpy; every "
+                      f"other workload sampled in per_config; host reports {os.cpu_count()} CPUs, "
+                      f"{cores} in this process's affinity (BLAS threads)",
+            "per_config": per, "oracle_seconds_sampled": total}
+
+
+# ---------------------------------------------------------------------------
+# Main
+# ---------------------------------------------------------------------------
 
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU: there is no multi-GPU path "
-              "(the score and write paths shard with no exchange)",
-              file=sys.stderr)
+              "(the score and write paths shard with no exchange)", file=sys.stderr)
         sys.exit(2)
-    if args.workloads:
-        workload_table(args)
-        return
 
+    import numpy as np
     import torch
     import lut_attention_scoring_amd as axr
     import workloads as W
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
     log("generating LLaMA-3.1-8B-shaped decode cache")
     w = W.llama_decode()
     B, Hkv, T, d = w["keys"].shape
     Hq = w["q"].shape[1]
+    G = Hq // Hkv
     b, bits = w["b"], w["sign_bits"]
     n = B * Hkv * T
     keys = w["keys"].to(dev)
     q = w["q"].to(dev)
+    del w
     packed = torch.empty(B, Hkv, T, d * b // 32, dtype=torch.int32, device=dev)
     norms = torch.empty(B, Hkv, T, dtype=torch.float32, device=dev)
     scores = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    axr.quantize_keys(keys, bits, b, packed=packed, norms=norms)
+    wbytes = n * write_bytes_per_key(d, b, keys.element_size())
+    sbytes = n * score_bytes_per_key(d, b, G)
+
+    if args.profile:
+        k = args.profile
+        if k in ("score_rotating", "score_resident"):
+            r = time_score(torch, axr, stream, q, packed, norms, bits, b, args.steps,
+                           min_copies=4 if k == "score_rotating" else 1) \
+                if k == "score_rotating" else None
+            if r is None:
+                ms = launches_ms(torch, stream,
+                                 lambda: axr.score(q, packed, norms, bits, b, out=scores),
+                                 args.steps)
+                r = {"us": ms * 1e3, "GB_per_s": sbytes / (ms * 1e6)}
+        elif k == "write":
+            r = time_write(torch, axr, stream, keys, bits, b, args.steps)
+        else:
+            del keys
+            if k == "qwen_score":
+                w = W.qwen_layer(0)
+                bb = 4
+            else:
+                w = W.long_context(b=4)
+                bb = 4
+            kk, qq = w["keys"].to(dev), w["q"].to(dev)
+            pk, nm = axr.quantize_keys(kk, w["sign_bits"], bb)
+            r = time_score(torch, axr, stream, qq, pk, nm, w["sign_bits"], bb, args.steps)
+        print(json.dumps({"profile": k, **r}), flush=True)
+        return
 
     def step():
         axr.quantize_keys(keys, bits, b, packed=packed, norms=norms)
         axr.score(q, packed, norms, bits, b, out=scores)
 
-    # The collector runs before the warmup, so that the GPU idles only for
-    # the synchronisation between the warmup and the timed steps.
-    log(f"warmup {args.warmup}, timing {args.steps} steps")
+    # Steps run untimed for settle_ms first: a write + score loop starting
+    # from an idle chip runs its first ~10 ms up to half slower while the
+    # clock ramps; then the warmup steps, then the timed steps with HIP events
+    # around each kernel (on the stream the kernels run on).
+    log(f"settle {args.settle_ms:.0f} ms, warmup {args.warmup}, timing {args.steps} steps")
     gc.collect()
     gc.disable()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.settle_ms * 1e-3:
+        for _ in range(16):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for e in ev:
+        e[0].record(stream)
+        axr.quantize_keys(keys, bits, b, packed=packed, norms=norms)
+        e[1].record(stream)
+        axr.score(q, packed, norms, bits, b, out=scores)
+        e[2].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gc.enable()
     ms_per_step = elapsed * 1e3 / args.steps
+    step_write_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    step_score_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
 
     def per_launch_ms(fn, reps):
         return launches_ms(torch, stream, fn, reps)
 
     log("per-kernel timing")
-    write_ms = per_launch_ms(lambda: axr.quantize_keys(keys, bits, b, packed=packed, norms=norms),
-                             args.steps)
-    score_ms = per_launch_ms(lambda: axr.score(q, packed, norms, bits, b, out=scores), args.steps)
+    write_hbm = time_write(torch, axr, stream, keys, bits, b, args.steps)
+    score_hbm = time_score(torch, axr, stream, q, packed, norms, bits, b, args.steps)
+    score_res_ms = per_launch_ms(lambda: axr.score(q, packed, norms, bits, b, out=scores),
+                                 args.steps)
 
     # Decode step on the same cache: one new key per (sequence, KV head)
     # appended at the last slot, then every sequence scored up to it.
     log("decode-step timing")
-    import numpy as np
     rng = np.random.default_rng(105)
     new_k = torch.from_numpy(rng.standard_normal((B, Hkv, d)).astype(np.float32)).to(
         keys.dtype).to(dev)
@@ -262,9 +523,6 @@ def main():
     decode_ms = per_launch_ms(decode_step, args.steps)
     fused_ms = per_launch_ms(
         lambda: axr.decode_step(q, new_k, bits, b, packed, norms, pos, out=scores), args.steps)
-
-    # The same step captured once in a HIP graph and replayed (one launch
-    # per step from the host).
     side = torch.cuda.Stream(dev)
     side.wait_stream(stream)
     with torch.cuda.stream(side):
@@ -278,8 +536,6 @@ def main():
     decode_graph_ms = per_launch_ms(graph.replay, args.steps)
     del graph
 
-    # Attention probabilities: scores with split-T softmax partials, then the
-    # row normalisation (scale 1/sqrt(d)); written over `scores`.
     log("softmax timing")
     lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
     ws = torch.empty(max(8, axr.score_softmax_workspace_bytes(B, Hq, Hkv, T, d, b)),
@@ -288,9 +544,7 @@ def main():
         lambda: axr.score_softmax(q, packed, norms, bits, b, out=scores, lse=lse, workspace=ws),
         args.steps)
 
-    # Score kernel alone on a cold cache: read 2 GiB between launches, which
-    # evicts the 136 MiB working set from the 256 MB Infinity Cache and L2
-    # without leaving dirty lines behind.
+    # Score kernel alone after 2 GiB of reads (cold cache, single launches).
     log("cold-cache score timing")
     flush = torch.ones(1 << 29, dtype=torch.float32, device=dev)
     flush_bytes = flush.numel() * flush.element_size()
@@ -307,48 +561,24 @@ def main():
     cold.sort()
     cold_ms = cold[len(cold) // 2]
 
-    # ... and back to back over three copies of the cache (3 x 136 MiB, more
-    # than the Infinity Cache holds): each launch's records, norms and scores
-    # were last touched two launches (~280 MB of traffic) earlier, so they
-    # come from HBM, without a single launch's start-up in the figure.
-    log("rotating-cache score timing")
-    copies = [(packed, norms, scores)] + [
-        (packed.clone(), norms.clone(), torch.empty_like(scores)) for _ in range(2)]
-    rot = [0]
-
-    def score_rotating():
-        pk, nm, sc = copies[rot[0] % 3]
-        rot[0] += 1
-        axr.score(q, pk, nm, bits, b, out=sc)
-
-    rotating_ms = per_launch_ms(score_rotating, 3 * (args.steps // 3) or 3)
-    # the bare stream with the score kernel's traffic, rotating the same way:
-    # three disjoint 109 MB regions of the key tensor in, the three score
-    # buffers out (the HBM-sourced ceiling for this kernel)
-    score_in_rot = n * (d * b // 8 + 4)
-    score_out_rot = n * 4 * (Hq // Hkv)
-    key_bytes = keys.view(torch.uint8).reshape(-1)
-
-    def stream_rotating():
-        r = rot[0] % 3
-        rot[0] += 1
-        axr.probe_read_write(key_bytes[r * score_in_rot:(r + 1) * score_in_rot], score_in_rot,
-                             copies[r][2], score_out_rot)
-
-    rotating_stream_ms = per_launch_ms(stream_rotating, 3 * (args.steps // 3) or 3)
-    del copies, key_bytes
-
-    # Achievable-bandwidth ceilings on this machine (include/axr_probe.h): a
-    # bare 2 GiB read stream, and streams with the score kernel's and the
-    # write kernel's traffic (read bytes, then write bytes, per block).
+    # Bare streams with the kernels' traffic (include/axr_probe.h): a 2 GiB
+    # read, the score kernel's (records + norms in, scores out) back to back
+    # on one region and cycling over four, and the write kernel's.
     log("bandwidth probes")
     psink = torch.zeros(4, dtype=torch.int32, device=dev)
     read_ms = per_launch_ms(lambda: axr.probe_read_stream(flush, psink), 10)
     score_in = n * (d * b // 8 + 4)
-    score_out = n * 4 * (Hq // Hkv)
+    score_out = n * 4 * G
     shaped_ms = per_launch_ms(lambda: axr.probe_read_write(keys, score_in, scores, score_out),
                               args.steps)
-    # and one with the write kernel's traffic (the keys in, records and norms out)
+    kb = keys.view(torch.uint8).reshape(-1)
+    nreg = 4
+    regions = [(kb[r * score_in:(r + 1) * score_in], torch.empty_like(scores))
+               for r in range(min(nreg, kb.numel() // score_in))]
+    rot_stream_ms = per_launch_ms(
+        Rotor(regions, lambda c: axr.probe_read_write(c[0], score_in, c[1], score_out)),
+        max(args.steps, len(regions)) // len(regions) * len(regions))
+    del regions, kb
     write_in = n * d * keys.element_size()
     write_out = n * (d * b // 8 + 4)
     wscratch = torch.empty(write_out, dtype=torch.uint8, device=dev)
@@ -367,17 +597,16 @@ def main():
         nm = torch.empty(nk, dtype=torch.float32, device=dev)
         qs = torch.from_numpy(W.isoquant_quaternions(dd)).to(dev)
         sb = W.sign_bits(dd)
-        kb = nk * (dd * 2 + dd * 3 // 8 + 4)
+        kbytes = nk * (dd * 2 + dd * 3 // 8 + 4)
         for name, fn in (
                 ("wht", lambda: axr.quantize_keys(ws_keys, sb, 3, packed=pk, norms=nm)),
                 ("isoquant_full", lambda: axr.quantize_keys_isoquant(ws_keys, qs, 3, True, pk, nm)),
                 ("isoquant_fast", lambda: axr.quantize_keys_isoquant(ws_keys, qs, 3, False, pk, nm))):
             t_ms = per_launch_ms(fn, args.steps)
-            wt[f"d{dd}_{name}"] = {"ms": t_ms, "GB_per_s": kb / (t_ms * 1e-3) / 1e9}
+            wt[f"d{dd}_{name}"] = {"us": t_ms * 1e3, "GB_per_s": kbytes / (t_ms * 1e6)}
         del ws_keys, pk, nm
 
-    # One-time sign-pattern selection: 200 candidates on 8 calibration layers
-    # (B=1, 2 KV heads, 16 query heads, 2048 tokens, b=4).
+    # One-time sign-pattern selection: 200 candidates on 8 calibration layers.
     log("sign-pattern selection timing")
     cal = W.calibration_samples()
     cal_k, cal_q = cal["keys"].to(dev), cal["q"].to(dev)
@@ -392,16 +621,12 @@ def main():
     gc.enable()
     del cal_k, cal_q
 
-    write_bytes_per_key = d * keys.element_size() + d * b // 8 + 4
-    score_bytes_per_key = d * b // 8 + 4 + 4 * (Hq // Hkv)
-    write_bytes = n * write_bytes_per_key
-    score_bytes = n * score_bytes_per_key
-    write_gbs = write_bytes / (write_ms * 1e-3) / 1e9
-    score_gbs = score_bytes / (score_ms * 1e-3) / 1e9
-    cold_gbs = score_bytes / (cold_ms * 1e-3) / 1e9
-    dominant = "write" if write_ms >= score_ms else "score"
-    dom_gbs = write_gbs if dominant == "write" else score_gbs
-    dom_bytes = write_bytes if dominant == "write" else score_bytes
+    del keys, packed, norms, scores, q
+    torch.cuda.empty_cache()
+    configs = None
+    if not args.no_configs:
+        log("every workload")
+        configs = configs_section(torch, axr, W, stream, args.steps)
 
     out = {
         "metric": METRIC,
@@ -418,45 +643,54 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama31_8b_gqa_decode_d128_b3", "batch": B, "kv_heads": Hkv,
                    "q_heads": Hq, "context": T, "d": d, "b": b, "key_dtype": "f16",
-                   "keys_per_step": n},
-        "roofline": {"kernel": f"{dominant}_kernel", "bound": "hbm",
-                     "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic(dominant),
-                     "bytes_per_launch": dom_bytes},
+                   "query_dtype": "f16", "keys_per_step": n,
+                   "arithmetic": "fp32 transform and norms, int32 fixed-point table sums",
+                   "settle_ms": args.settle_ms},
+        "roofline": {"kernel": "score", "source": f"HBM ({score_hbm['copies']} rotating "
+                                                  "copies of the cache)",
+                     "bound": "hbm", "achieved": round(score_hbm["GB_per_s"], 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(score_hbm["GB_per_s"] / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic("score"), "bytes_per_launch": sbytes,
+                     "us": score_hbm["us"]},
+        "roofline_write": {"kernel": "write", "source": f"HBM ({write_hbm['copies']} rotating "
+                                                        "copies of the keys)",
+                           "bound": "hbm", "achieved": round(write_hbm["GB_per_s"], 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(write_hbm["GB_per_s"] / HBM_PEAK_GBS, 4),
+                           "traffic": counter_traffic("write"), "bytes_per_launch": wbytes,
+                           "us": write_hbm["us"]},
+        "step_kernels": {"write_us": step_write_ms * 1e3, "score_us": step_score_ms * 1e3,
+                         "note": "HIP events around each kernel inside the timed steps; the "
+                                 "score kernel there reads records the write kernel has just "
+                                 "written"},
         "ceiling": {
             "read_stream_GB_per_s": flush_bytes / (read_ms * 1e-3) / 1e9,
             "read_stream_bytes": flush_bytes,
-            "score_shaped_stream_GB_per_s": (score_in + score_out) / (shaped_ms * 1e-3) / 1e9,
-            "score_shaped_stream_ms": shaped_ms,
-            "score_frac_of_shaped_stream": shaped_ms / score_ms,
-            "score_shaped_stream_rotating_GB_per_s":
-                (score_in_rot + score_out_rot) / (rotating_stream_ms * 1e-3) / 1e9,
-            "score_shaped_stream_rotating_ms": rotating_stream_ms,
-            "score_rotating_frac_of_rotating_stream": rotating_stream_ms / rotating_ms,
-            "write_shaped_stream_GB_per_s": (write_in + write_out) / (wshaped_ms * 1e-3) / 1e9,
-            "write_shaped_stream_ms": wshaped_ms,
-            "write_frac_of_shaped_stream": wshaped_ms / write_ms,
+            "score_shaped_stream_cache_resident_us": shaped_ms * 1e3,
+            "score_shaped_stream_rotating_us": rot_stream_ms * 1e3,
+            "score_shaped_stream_rotating_GB_per_s": sbytes / (rot_stream_ms * 1e6),
+            "score_hbm_frac_of_rotating_stream": rot_stream_ms / (score_hbm["us"] * 1e-3),
+            "write_shaped_stream_us": wshaped_ms * 1e3,
+            "write_shaped_stream_GB_per_s": wbytes / (wshaped_ms * 1e6),
+            "write_frac_of_shaped_stream": wshaped_ms / (write_hbm["us"] * 1e-3),
         },
         "kernels": {
-            "write": {"ms": write_ms, "keys_per_s": n / (write_ms * 1e-3),
-                      "GB_per_s": write_gbs, "frac_hbm": write_gbs / HBM_PEAK_GBS,
-                      "bytes_per_key": write_bytes_per_key,
-                      "traffic": counter_traffic("write")},
-            "score": {"ms": score_ms, "keys_per_s": n / (score_ms * 1e-3),
-                      "head_scores_per_s": n * (Hq // Hkv) / (score_ms * 1e-3),
-                      "GB_per_s": score_gbs, "frac_hbm": score_gbs / HBM_PEAK_GBS,
-                      "bytes_per_key": score_bytes_per_key,
-                      "traffic": counter_traffic("score")},
-            "score_cold_cache": {"ms_median": cold_ms, "keys_per_s": n / (cold_ms * 1e-3),
-                                 "GB_per_s": cold_gbs, "frac_hbm": cold_gbs / HBM_PEAK_GBS},
-            "score_rotating_caches": {
-                "ms": rotating_ms, "keys_per_s": n / (rotating_ms * 1e-3),
-                "GB_per_s": score_bytes / (rotating_ms * 1e6),
-                "frac_hbm": score_bytes / (rotating_ms * 1e6) / HBM_PEAK_GBS,
-                "note": "back to back over 3 copies of the cache (408 MiB > 256 MB Infinity Cache)"},
-            "score_softmax": {"ms": softmax_ms, "keys_per_s": n / (softmax_ms * 1e-3),
-                              "note": "score kernel with split-T partials + row normalisation"},
+            "write_hbm": write_hbm,
+            "score_hbm": score_hbm,
+            "score_cache_resident": {
+                "us": score_res_ms * 1e3, "keys_per_s": n / (score_res_ms * 1e-3),
+                "GB_per_s": sbytes / (score_res_ms * 1e6),
+                "frac_of_peak_cache_resident": sbytes / (score_res_ms * 1e6) / HBM_PEAK_GBS,
+                "note": "back to back on one copy: the 136 MiB working set is served from the "
+                        "256 MB Infinity Cache, not HBM"},
+            "score_cold_cache": {"us_median": cold_ms * 1e3, "keys_per_s": n / (cold_ms * 1e-3),
+                                 "GB_per_s": sbytes / (cold_ms * 1e6),
+                                 "frac_hbm": sbytes / (cold_ms * 1e6) / HBM_PEAK_GBS,
+                                 "note": "single launches after 2 GiB of reads"},
+            "score_softmax": {"us": softmax_ms * 1e3, "keys_per_s": n / (softmax_ms * 1e-3),
+                              "note": "score kernel with split-T partials + row normalisation, "
+                                      "back to back"},
             "write_transforms_b3": wt,
             "sign_selection": {"ms": sel_ms, "candidates": len(cands),
                                "calibration_samples": int(cal["keys"].shape[0]),
@@ -465,17 +699,17 @@ def main():
                                "objective_default": float(sel_obj[0]),
                                "objective_chosen": float(sel_obj[sel_idx]),
                                "objective_worst": float(sel_obj.max())},
-            "decode_step": {"ms": decode_ms, "graph_replay_ms": decode_graph_ms,
-                            "fused_ms": fused_ms,
-                            "append_ms": append_ms,
+            "decode_step": {"us": decode_ms * 1e3, "graph_replay_us": decode_graph_ms * 1e3,
+                            "fused_us": fused_ms * 1e3, "append_us": append_ms * 1e3,
                             "appended_keys": B * Hkv, "scored_keys": n,
                             "note": "append one key per (sequence, KV head) + ragged score; "
-                                    "fused = one launch (axr_decode_step)"},
+                                    "fused = one launch (axr_decode_step); back to back"},
         },
+        "configs": configs,
     }
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(w)
+        log("timing the CPU oracle on bounded samples")
+        out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 
 
