@@ -37,6 +37,8 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "axr.h"
 #include "axr_device.h"
 #include "axr_internal.h"
@@ -68,6 +70,26 @@ __device__ __forceinline__ uint32_t quad_reduce_scatter(const uint32_t (&a)[4]) 
   const uint32_t k0 = dpp_add<2>(a[0], a[2]);   // heads u and u^1 (+ partner u^2)
   const uint32_t k1 = dpp_add<2>(a[1], a[3]);
   return dpp_add<1>(k0, k1);                    // head u
+}
+
+// The same for fp32 partial sums (v_add_f32 with a DPP source).
+template <int M>
+__device__ __forceinline__ float dpp_addf(float k, float s) {
+  if constexpr (M == 1) {
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "+v"(k) : "v"(s));
+  } else {
+    static_assert(M == 2, "quad distances only");
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+        : "+v"(k) : "v"(s));
+  }
+  return k;
+}
+
+__device__ __forceinline__ float quad_reduce_scatter(const float (&a)[4]) {
+  const float k0 = dpp_addf<2>(a[0], a[2]);
+  const float k1 = dpp_addf<2>(a[1], a[3]);
+  return dpp_addf<1>(k0, k1);
 }
 
 // Running (max, sum of exp(x - max)) of a stream of finite values x, one
@@ -129,7 +151,12 @@ __device__ __forceinline__ float row_elem(const void* p, int dtype, size_t i) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-template <int D, int BITS, int P>
+// Table shapes.  SG = false: int32 fixed-point entries for every field value
+// (the mirrored half written by negation).  SG = true: fp32 entries for the
+// fields whose top bit is clear only; a field f with the top bit set reads the
+// entry of its mirror ~f and negates it (the codebook's symmetry makes the two
+// exact negatives), which halves the table so that pairs of 4-bit fields fit.
+template <int D, int BITS, int P, bool SG = false>
 struct ScoreShape {
   static constexpr int LPK = D / 32;            // lanes per key
   static constexpr int KPG = 16 / LPK;          // keys per 16-lane group
@@ -137,9 +164,10 @@ struct ScoreShape {
   static constexpr int WL = BITS;               // record words per lane (32 coords)
   static constexpr int W = D * BITS / 32;       // record words per key
   static constexpr int FB = P * BITS;           // field bits per group
-  static constexpr int NE = 1 << FB;            // entries per group
+  static constexpr int NE = 1 << FB;            // field values per group
+  static constexpr int NES = SG ? NE / 2 : NE;  // entries stored per group
   static constexpr int NV = 32 / P;             // groups per lane
-  static constexpr int ROWS_U = (NV / 16) * NE; // 256-byte rows per lane chunk
+  static constexpr int ROWS_U = (NV / 16) * NES;  // 256-byte rows per lane chunk
   static constexpr int TBYTES = 256 * LPK * ROWS_U;  // bytes per 4-head table
 };
 
@@ -190,13 +218,14 @@ __device__ __forceinline__ void buffer_load_words(uint32_t (&dst)[WL], __amdgpu_
 // partials, or the fused decode step's new key.
 enum ScoreMode { kPlain = 0, kLse = 1, kDecode = 2 };
 
-template <int D, int BITS, int P, int NT, int NTHREADS, int MODE>
+template <int D, int BITS, int P, int NT, int NTHREADS, int MODE, bool SG>
 __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict__ q, int qdt,
                                                        const uint32_t* __restrict__ packed,
                                                        const float* __restrict__ norms,
                                                        float* __restrict__ scores,
                                                        ScoreParams prm) {
-  using S = ScoreShape<D, BITS, P>;
+  using S = ScoreShape<D, BITS, P, SG>;
+  static_assert(!SG || S::LPK == 4, "signed half tables are built for d = 128");
   constexpr int GB = 4 * NT;                    // heads per block (some may be padding)
   constexpr int L = 1 << BITS;                  // codebook levels
   constexpr int HL = L / 2;
@@ -204,9 +233,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   // NT tables of S::TBYTES bytes, q' [GB][D] and the head scales.
   __shared__ int4 lut[NT * (S::TBYTES / 16)];
   __shared__ float qs[GB][D];
-  __shared__ float hscale[GB], hinv[GB];       // 2^e and 2^-e of each head's
-  __shared__ float hscale2[GB], hinv2[GB];     // scale, as two exact factors
-  __shared__ float cent[16];
+  __shared__ float hinv[GB], hinv2[GB];        // 2^-e of each head's scale, as two exact factors
 
   const int tid = threadIdx.x;
   const int tile = blockIdx.x % prm.tiles;
@@ -291,13 +318,13 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   //    the 32-bit sums, which wrap, end exact.
   constexpr int R = D / 64;
   float v[R];
+  uint32_t raw[R];
   if (wave < GB) {
     // All loads of the head are issued before the first wait (one memory
     // round trip); the sign words are kernel arguments read at uniform
     // indices, so they come from scalar registers.
     const int g = wave < nvalid ? wave : 0;   // padding heads load head 0, zeroed below
     const size_t qrow = (static_cast<size_t>(bi) * prm.Hq + h0 + g) * D + lane;
-    uint32_t raw[R];
     if (qdt == AXR_F32) {
 #pragma unroll
       for (int r = 0; r < R; ++r) raw[r] = static_cast<const uint32_t*>(q)[qrow + 64 * r];
@@ -305,6 +332,24 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 #pragma unroll
       for (int r = 0; r < R; ++r) raw[r] = static_cast<const uint16_t*>(q)[qrow + 64 * r];
     }
+  }
+
+  // The first PD batches of record loads go out right behind the query loads
+  // (which start the critical path and should not queue behind them), so
+  // that their memory latency overlaps the query transform and the table
+  // build.
+  uint32_t wq[PD][S::WL];
+  float nq[PD];
+  uint32_t ks[PD];                              // unit of each batch in flight
+#pragma unroll
+  for (int pd = 0; pd < PD; ++pd) {
+    ks[pd] = static_cast<uint32_t>(pd * NW) + wave_s;
+    buffer_load_words<S::WL>(wq[pd], rrec, vrec + ks[pd] * (S::KPW * REC_BYTES), 0);
+    nq[pd] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rnrm, vnrm + ks[pd] * (S::KPW * 4u), 0, 0));
+  }
+
+  if (wave < GB) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float x;
@@ -322,11 +367,6 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
       v[r] = wave < nvalid ? __uint_as_float(__float_as_uint(x) ^ neg) : 0.0f;
     }
   }
-  if (tid == 0) {
-#pragma unroll
-    for (int i = 0; i < L; ++i) cent[i] = prm.centroid[i];
-  }
-
   if (wave < GB) {
     const int g = wave;
     wht_row<R>(v, lane);
@@ -335,7 +375,6 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       v[r] *= inv_sqrt_d;
-      qs[g][lane + 64 * r] = v[r];
       sa += fabsf(v[r]);
     }
     sa += lane_xor<1>(sa);
@@ -344,19 +383,24 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
     sa += lane_xor<8>(sa);
     sa += lane_xor<16>(sa);
     sa += lane_xor<32>(sa);
+    // The butterfly leaves the same sum in every lane (each step adds the
+    // same two values, in either order), so every lane picks the same scale
+    // and stores its coordinates of q' already multiplied by it (exact: a
+    // power of two, applied as two factors that never leave fp32's range).
+    const float cmax = fabsf(prm.centroid[L - 1]);
+    const float f = sa * cmax * 1.0001f;
+    int e = 0;
+    if (f > 0.0f) frexpf(f, &e);                // f < 2^e
+    int sh = SG ? 0 : 31 - e;                   // fp32 entries need no fixed point
+    // up to 2^252 for tiny queries, applied as two powers of two that are
+    // each representable (the second is 1 unless sh > 126)
+    sh = sh > 252 ? 252 : (sh < -126 ? -126 : sh);
+    const int sh1 = sh > 126 ? 126 : sh;
+    const float s1 = ldexpf(1.0f, sh1), s2 = ldexpf(1.0f, sh - sh1);
+#pragma unroll
+    for (int r = 0; r < R; ++r) qs[g][lane + 64 * r] = (v[r] * s1) * s2;
     if (lane == 0) {
-      const float cmax = fabsf(prm.centroid[L - 1]);
-      const float f = sa * cmax * 1.0001f;
-      int e = 0;
-      if (f > 0.0f) frexpf(f, &e);              // f < 2^e
-      int sh = 31 - e;
-      // up to 2^252 for tiny queries, applied as two powers of two that are
-      // each representable (the second is 1 unless sh > 126)
-      sh = sh > 252 ? 252 : (sh < -126 ? -126 : sh);
-      const int sh1 = sh > 126 ? 126 : sh;
-      hscale[g] = ldexpf(1.0f, sh1);
       hinv[g] = ldexpf(1.0f, -sh1);
-      hscale2[g] = ldexpf(1.0f, sh - sh1);
       hinv2[g] = ldexpf(1.0f, sh1 - sh);
     }
   }
@@ -434,20 +478,6 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
     }
   }
 
-  // Issue the first PD batches of record loads now: after the query loads
-  // (which start the critical path and should not queue behind them) and
-  // before the table build, which they overlap.
-  uint32_t wq[PD][S::WL];
-  float nq[PD];
-  uint32_t ks[PD];                              // unit of each batch in flight
-#pragma unroll
-  for (int pd = 0; pd < PD; ++pd) {
-    ks[pd] = static_cast<uint32_t>(pd * NW) + wave_s;
-    buffer_load_words<S::WL>(wq[pd], rrec, vrec + ks[pd] * (S::KPW * REC_BYTES), 0);
-    nq[pd] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           rnrm, vnrm + ks[pd] * (S::KPW * 4u), 0, 0));
-  }
-
   // 2. the tables, one 16-byte entry (4 heads) per (lane chunk u, group v,
   //    field f).  The codebook is symmetric (c[L-1-k] = -c[k]), so the entry
   //    of the fully mirrored field is the negation: each task rounds the
@@ -455,7 +485,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   //    entry is the sum of its two rounded coordinate terms.
   {
     auto slot_of = [](int uu, int vv, int ff) {
-      return 16 * (uu * S::ROWS_U + (vv / 16) * S::NE + ff) + ((vv + S::KPG * uu) & 15);
+      return 16 * (uu * S::ROWS_U + (vv / 16) * S::NES + ff) + ((vv + S::KPG * uu) & 15);
     };
     constexpr int HALF_NE = S::NE / 2;           // fields with the top bit clear
     constexpr int GROUPS = NT * S::LPK * S::NV;  // (table, chunk, group) triples
@@ -464,34 +494,48 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
     // fastest: the 16 lanes of a quarter-wave write 16 distinct LDS columns.
     constexpr int FSPLIT = NTHREADS / GROUPS < 1 ? 1
                            : (NTHREADS / GROUPS < HALF_NE ? NTHREADS / GROUPS : HALF_NE);
+    static_assert(GROUPS % 64 == 0, "a wave's 64 items share their field index");
     for (int item = tid; item < GROUPS * FSPLIT; item += NTHREADS) {
       const int vv = item % S::NV;
       const int uu = (item / S::NV) % S::LPK;
       const int t4 = (item / (S::NV * S::LPK)) % NT;
-      const int f0 = item / GROUPS;
+      // wave-uniform, so the centroids below come from the kernel arguments
+      const int f0 = __builtin_amdgcn_readfirstlane(item / GROUPS);
       const int j = 32 * uu + P * vv;
       int4* tab = lut + t4 * (S::TBYTES / 16);
       // With four lanes per key, component i of chunk u's entries holds head
       // u ^ i (see quad_reduce_scatter); otherwise heads are in order.  The
-      // coordinates are read in that order, q'_j 2^e (exact: the scale is a
-      // power of two).
+      // coordinates are read in that order, q'_j 2^e (stored scaled).
       const int pu = S::LPK == 4 ? (uu & 3) : 0;
       float qa[4], qb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int g = 4 * t4 + (i ^ pu);
-        qa[i] = (qs[g][j] * hscale[g]) * hscale2[g];
-        qb[i] = P == 2 ? (qs[g][j + P - 1] * hscale[g]) * hscale2[g] : 0.0f;
+        qa[i] = qs[g][j];
+        qb[i] = P == 2 ? qs[g][j + P - 1] : 0.0f;
       }
       for (int f = f0; f < HALF_NE; f += FSPLIT) {
+        const float ca = prm.centroid[f & (L - 1)];
+        const float cb = P == 2 ? prm.centroid[f >> BITS] : 0.0f;
+        if constexpr (SG) {
+          // fp32 entry: the two coordinate terms, rounded, then their sum
+          float ef[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float ta = mul_rounded(qa[i], ca);
+            ef[i] = P == 2 ? ta + mul_rounded(qb[i], cb) : ta;
+          }
+          tab[slot_of(uu, vv, f)] = make_int4(__float_as_int(ef[0]), __float_as_int(ef[1]),
+                                              __float_as_int(ef[2]), __float_as_int(ef[3]));
+          continue;
+        }
         int e[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (P == 1) {
-            e[i] = __float2int_rn(qa[i] * cent[f]);
+            e[i] = __float2int_rn(qa[i] * ca);
           } else {
-            e[i] = __float2int_rn(qa[i] * cent[f & (L - 1)]) +
-                   __float2int_rn(qb[i] * cent[f >> BITS]);
+            e[i] = __float2int_rn(qa[i] * ca) + __float2int_rn(qb[i] * cb);
           }
         }
         const int fm = (S::NE - 1) ^ f;            // every field mirrored
@@ -508,10 +552,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   for (int st = 0; st < S::NV; ++st) {
     const int vv = (st + kslot) % S::NV;
     boff[st] = static_cast<uint32_t>(
-        256 * (u * S::ROWS_U + (vv / 16) * S::NE) + 16 * ((vv + S::KPG * u) & 15));
+        256 * (u * S::ROWS_U + (vv / 16) * S::NES) + 16 * ((vv + S::KPG * u) & 15));
   }
   const uint32_t rot = static_cast<uint32_t>(kslot * S::FB);
-  const uint32_t fmask = ((1u << S::FB) - 1u) << 8;
+  const uint32_t fmask = static_cast<uint32_t>(S::NES - 1) << 8;
   // Scores of this block's heads through a raw buffer resource (uniform
   // base: the block's first head row); each lane stores head u (and u + 4)
   // at a fixed per-lane offset plus a per-batch scalar offset.
@@ -594,22 +638,33 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
         rotate_right<S::WL>(w[il], rot);
       }
 
-      uint32_t acc[IL][GB];
+      using Acc = typename std::conditional<SG, float, uint32_t>::type;
+      Acc acc[IL][GB];
 #pragma unroll
       for (int il = 0; il < IL; ++il)
 #pragma unroll
-        for (int g = 0; g < GB; ++g) acc[il][g] = 0u;
+        for (int g = 0; g < GB; ++g) acc[il][g] = Acc(0);
       // The lookups of CH steps are issued before any of their sums, so a
       // wave keeps CH * NT * IL table reads in flight.
 #pragma unroll
       for (int st0 = 0; st0 < S::NV; st0 += CH) {
         int4 e[CH][IL][NT];
+        float sg[CH][IL];                         // +-1: field read directly or mirrored
 #pragma unroll
         for (int sc = 0; sc < CH; ++sc) {
 #pragma unroll
           for (int il = 0; il < IL; ++il) {
-            const uint32_t addr = and_or(
-                field_shl8_raw<S::WL>(w[il], (st0 + sc) * S::FB, S::FB), fmask, boff[st0 + sc]);
+            const uint32_t x = field_shl8_raw<S::WL>(w[il], (st0 + sc) * S::FB, S::FB);
+            uint32_t addr;
+            if constexpr (SG) {
+              // m = all ones when the field's top bit (bit 8 + FB - 1 of x) is
+              // set: the entry of the mirrored field ~f, negated
+              const int32_t m = static_cast<int32_t>(x << (24 - S::FB)) >> 31;
+              addr = and_or(x ^ static_cast<uint32_t>(m), fmask, boff[st0 + sc]);
+              sg[sc][il] = __uint_as_float((static_cast<uint32_t>(m) & 0x80000000u) | 0x3F800000u);
+            } else {
+              addr = and_or(x, fmask, boff[st0 + sc]);
+            }
 #pragma unroll
             for (int t4 = 0; t4 < NT; ++t4)
               e[sc][il][t4] = *reinterpret_cast<const int4*>(lut_bytes + addr + t4 * S::TBYTES);
@@ -621,10 +676,17 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
           for (int il = 0; il < IL; ++il) {
 #pragma unroll
             for (int t4 = 0; t4 < NT; ++t4) {
-              acc[il][4 * t4 + 0] += static_cast<uint32_t>(e[sc][il][t4].x);
-              acc[il][4 * t4 + 1] += static_cast<uint32_t>(e[sc][il][t4].y);
-              acc[il][4 * t4 + 2] += static_cast<uint32_t>(e[sc][il][t4].z);
-              acc[il][4 * t4 + 3] += static_cast<uint32_t>(e[sc][il][t4].w);
+              if constexpr (SG) {
+                acc[il][4 * t4 + 0] = fmaf(__int_as_float(e[sc][il][t4].x), sg[sc][il], acc[il][4 * t4 + 0]);
+                acc[il][4 * t4 + 1] = fmaf(__int_as_float(e[sc][il][t4].y), sg[sc][il], acc[il][4 * t4 + 1]);
+                acc[il][4 * t4 + 2] = fmaf(__int_as_float(e[sc][il][t4].z), sg[sc][il], acc[il][4 * t4 + 2]);
+                acc[il][4 * t4 + 3] = fmaf(__int_as_float(e[sc][il][t4].w), sg[sc][il], acc[il][4 * t4 + 3]);
+              } else {
+                acc[il][4 * t4 + 0] += static_cast<uint32_t>(e[sc][il][t4].x);
+                acc[il][4 * t4 + 1] += static_cast<uint32_t>(e[sc][il][t4].y);
+                acc[il][4 * t4 + 2] += static_cast<uint32_t>(e[sc][il][t4].z);
+                acc[il][4 * t4 + 3] += static_cast<uint32_t>(e[sc][il][t4].w);
+              }
             }
           }
         }
@@ -638,19 +700,23 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
           // lane u of the key ends with head u (and u + 4 when NT = 2)
 #pragma unroll
           for (int t4 = 0; t4 < NT; ++t4) {
-            const uint32_t a4[4] = {acc[il][4 * t4], acc[il][4 * t4 + 1], acc[il][4 * t4 + 2],
-                                    acc[il][4 * t4 + 3]};
-            const uint32_t tot = quad_reduce_scatter(a4);
-            const float sv =
-                (nk[il] * (static_cast<float>(static_cast<int32_t>(tot)) * ginv_u[t4])) *
-                ginv2_u[t4];
+            const Acc a4[4] = {acc[il][4 * t4], acc[il][4 * t4 + 1], acc[il][4 * t4 + 2],
+                               acc[il][4 * t4 + 3]};
+            const Acc tot = quad_reduce_scatter(a4);
+            float sv;
+            if constexpr (SG) {
+              sv = nk[il] * tot;
+            } else {
+              sv = (nk[il] * (static_cast<float>(static_cast<int32_t>(tot)) * ginv_u[t4])) *
+                   ginv2_u[t4];
+            }
             if (valid && 4 * t4 + u < nvalid) {
               __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), rsc,
                                                     vsc[t4], tb_rel * 4u, 0);
             }
             if (want_lse && valid) lse_push(sm_m[t4], sm_l[t4], mul_rounded(sv, lse_scale));
           }
-        } else {
+        } else if constexpr (!SG) {
           // sum over the LPK lanes of the key (exact integer sums)
 #pragma unroll
           for (int g = 0; g < GB; ++g) {
@@ -705,8 +771,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 
 constexpr int kLdsBudget = 128 * 1024;
 
-template <int D, int BITS, int P>
-constexpr int table_bytes(int NT) { return NT * ScoreShape<D, BITS, P>::TBYTES; }
+template <int D, int BITS, int P, bool SG = false>
+constexpr int table_bytes(int NT) { return NT * ScoreShape<D, BITS, P, SG>::TBYTES; }
 
 // Pairs when the pair table fits the LDS budget, else single coordinates.
 template <int D, int BITS, int NT>
@@ -715,18 +781,23 @@ constexpr int pick_p() { return table_bytes<D, BITS, 2>(NT) <= kLdsBudget ? 2 : 
 template <int D, int BITS, int NT>
 constexpr bool fits() { return table_bytes<D, BITS, pick_p<D, BITS, NT>()>(NT) <= kLdsBudget; }
 
-template <int D, int BITS, int NT>
+// 4-bit pairs at d = 128 as a signed half table (128 KiB for four heads);
+// elsewhere the int32 tables of pick_p.
+template <int D, int BITS>
+constexpr bool signed_pairs() { return D == 128 && BITS == 4; }
+
+template <int D, int BITS, int NT, bool SG>
 int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms, int B,
               ScoreParams p, float* scores, hipStream_t s, ScoreParams* plan) {
-  constexpr int P = pick_p<D, BITS, NT>();
-  constexpr int tbytes = table_bytes<D, BITS, P>(NT);
+  constexpr int P = SG ? 2 : pick_p<D, BITS, NT>();
+  constexpr int tbytes = table_bytes<D, BITS, P, SG>(NT);
   constexpr int bytes = tbytes + 4 * NT * D * 4 + 2 * 4 * NT * 4;  // + q' + scales
   static_assert(tbytes <= kLdsBudget, "table exceeds the LDS budget");
   // 1024-thread blocks, except the single-coordinate two-table case whose
   // registers need 512-thread blocks.
   constexpr int NTHREADS = (P == 1 && NT == 2) ? 512 : 1024;
   static_assert(bytes <= 160 * 1024, "LDS per block exceeded");
-  using S = ScoreShape<D, BITS, P>;
+  using S = ScoreShape<D, BITS, P, SG>;
   constexpr int KPB = (NTHREADS / 64) * S::KPW;
   p.heads_per_block = 4 * NT;
   p.head_groups = (p.G + 4 * NT - 1) / (4 * NT);
@@ -751,26 +822,33 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
   }
   const dim3 g(static_cast<unsigned>(grid)), blk(NTHREADS);
   if (mode == kDecode) {
-    hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kDecode>), g, blk, 0, s, q, qdt,
-                       packed, norms, scores, p);
+    hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kDecode, SG>), g, blk, 0, s, q,
+                       qdt, packed, norms, scores, p);
   } else if (mode == kLse) {
-    hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kLse>), g, blk, 0, s, q, qdt,
+    hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kLse, SG>), g, blk, 0, s, q, qdt,
                        packed, norms, scores, p);
   } else {
-    hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kPlain>), g, blk, 0, s, q, qdt,
-                       packed, norms, scores, p);
+    hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kPlain, SG>), g, blk, 0, s, q,
+                       qdt, packed, norms, scores, p);
   }
   return static_cast<int>(hipGetLastError());
 }
 
 // Eight heads per block when G >= 8 and both tables fit; otherwise four.
+// The signed half table takes four heads per block (a G = 8 row is two
+// blocks, each reading the records).
 template <int D, int BITS>
 int launch_b(const void* q, int qdt, const uint32_t* packed, const float* norms, int B,
              const ScoreParams& p, float* scores, hipStream_t s, ScoreParams* plan) {
-  if constexpr (fits<D, BITS, 2>()) {
-    if (p.G >= 8) return launch_nt<D, BITS, 2>(q, qdt, packed, norms, B, p, scores, s, plan);
+  if constexpr (signed_pairs<D, BITS>()) {
+    return launch_nt<D, BITS, 1, true>(q, qdt, packed, norms, B, p, scores, s, plan);
+  } else {
+    if constexpr (fits<D, BITS, 2>()) {
+      if (p.G >= 8)
+        return launch_nt<D, BITS, 2, false>(q, qdt, packed, norms, B, p, scores, s, plan);
+    }
+    return launch_nt<D, BITS, 1, false>(q, qdt, packed, norms, B, p, scores, s, plan);
   }
-  return launch_nt<D, BITS, 1>(q, qdt, packed, norms, B, p, scores, s, plan);
 }
 
 template <int D>
