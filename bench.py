@@ -148,7 +148,7 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the every-workload section")
     ap.add_argument("--profile", choices=["score_rotating", "score_resident", "write",
-                                          "qwen_score", "long_score_b4"],
+                                          "qwen_score", "long_score_b4", "write_sweep"],
                     help="run only this kernel's timed loop and print its figure")
     return ap.parse_args()
 
@@ -303,19 +303,45 @@ def configs_section(torch, axr, W, stream, reps):
     torch.cuda.empty_cache()
     log("configs: long context done")
 
-    # write sweep: 32768 tokens x 8 KV heads, d x b (the keys do not depend on b)
+    out["write_sweep_t32768x8"] = write_sweep_section(torch, axr, W, stream, reps)
+    log("configs: write sweep done")
+    return out
+
+
+def time_shaped_stream(torch, axr, stream, in_bytes, out_bytes, reps):
+    """The bare read-then-write stream probe with the given traffic, cycling
+    over enough disjoint regions that every launch reads from HBM."""
+    dev = torch.device("cuda:0")
+    k = n_copies(in_bytes + out_bytes, min_copies=2)
+    ins = [torch.empty(in_bytes, dtype=torch.uint8, device=dev) for _ in range(k)]
+    outs = [torch.empty(out_bytes, dtype=torch.uint8, device=dev) for _ in range(k)]
+    rot = Rotor(list(zip(ins, outs)), lambda c: axr.probe_read_write(c[0], in_bytes, c[1],
+                                                                    out_bytes))
+    ms = launches_ms(torch, stream, rot, max(reps, k) // k * k)
+    del ins, outs
+    return ms
+
+
+def write_sweep_section(torch, axr, W, stream, reps):
+    """Write kernel on the nine sweep cells (32768 tokens x 8 KV heads of bf16
+    keys, d x b; the keys do not depend on b), each beside the bare stream with
+    the same traffic (keys in, records and norms out), both from HBM."""
+    dev = torch.device("cuda:0")
     ws = {}
     for d in (128, 256, 512):
         w = W.write_sweep(d=d, b=3)
         keys, bits = w["keys"].to(dev), w["sign_bits"]
         del w
+        n = keys.numel() // d
         for b in (2, 3, 4):
-            ws[f"d{d}_b{b}"] = time_write(torch, axr, stream, keys, bits, b, reps)
+            r = time_write(torch, axr, stream, keys, bits, b, reps)
+            st = time_shaped_stream(torch, axr, stream, n * d * 2, n * (d * b // 8 + 4), reps)
+            r["shaped_stream_us"] = st * 1e3
+            r["frac_of_shaped_stream"] = st * 1e3 / r["us"]
+            ws[f"d{d}_b{b}"] = r
         del keys
         torch.cuda.empty_cache()
-    out["write_sweep_t32768x8"] = ws
-    log("configs: write sweep done")
-    return out
+    return ws
 
 
 # ---------------------------------------------------------------------------
@@ -435,6 +461,12 @@ def main():
 
     if args.profile:
         k = args.profile
+        if k == "write_sweep":
+            del keys, q, packed, norms, scores
+            torch.cuda.empty_cache()
+            print(json.dumps({"profile": k, **write_sweep_section(torch, axr, W, stream,
+                                                                  args.steps)}), flush=True)
+            return
         if k in ("score_rotating", "score_resident"):
             r = time_score(torch, axr, stream, q, packed, norms, bits, b, args.steps,
                            min_copies=4 if k == "score_rotating" else 1) \

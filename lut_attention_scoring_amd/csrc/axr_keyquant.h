@@ -19,6 +19,7 @@
 namespace axr {
 
 typedef _Float16 half2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 
 // One butterfly stage across lanes at distance M (see the file comment):
 // x <- x + m * x[lane ^ M].  Distances 1, 2 and 8 are single v_fmac_f32 with a
@@ -210,11 +211,11 @@ struct WhtLane {
     } else if constexpr (DT == AXR_BF16) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
+        const bf16x2_v b2 = __builtin_bit_cast(bf16x2_v, raw[i]);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(b2, b2, ss, false);
         const uint32_t f = raw[i] ^ xm[i];
         const float lo = __uint_as_float(f << 16);
         const float hi = __uint_as_float(f & 0xFFFF0000u);
-        ss = fmaf(lo, lo, ss);
-        ss = fmaf(hi, hi, ss);
         x[2 * i] = lo + hi;
         x[2 * i + 1] = lo - hi;
       }
@@ -265,24 +266,26 @@ __device__ __forceinline__ void quantize_lane(const float (&x)[32], const float 
 
 // The 4-bit index of each of a lane's 32 coordinates from the cell table:
 // u = z kc + kCellMid (kc = K / ||k||, K the table's scale) falls in cell c,
-// which holds cnt thresholds below it and at most one more, nxt, inside it;
-// the index is cnt + (z > nxt ||k||), the number of thresholds strictly
-// below z.  Indices fill the record words a nibble at a time, highest
-// coordinate first.
-__device__ __forceinline__ void quantize_cells(const float (&x)[32], float kc, float nrm,
+// which holds cnt thresholds below it and at most one more inside it, at
+// position un = t K + kCellMid on the same scale; the index is
+// cnt + (u > un), the number of thresholds strictly below z (z > t ||k||
+// taken on the cell scale, where the rounding of u and un is ~2^-17 of a
+// cell, a few 1e-7 of a threshold gap).  The host keeps |u - kCellMid| two
+// cells short of the table's ends for every key whose norm lies in the
+// table's range (the only keys that get here), and a non-finite u converts
+// to 0, so c needs no clamp.  Indices fill the record words a nibble at a
+// time, highest coordinate first.
+__device__ __forceinline__ void quantize_cells(const float (&x)[32], float kc,
                                                const uint2* cells, uint32_t (&words)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) words[i] = 0u;
 #pragma unroll
   for (int r = 31; r >= 0; --r) {
-    const float z = x[r];
-    const float u = fmaf(z, kc, kCellMid);
+    const float u = fmaf(x[r], kc, kCellMid);
     uint32_t c;
     asm("v_cvt_u32_f32 %0, %1" : "=v"(c) : "v"(u));   // saturating: < 0 -> 0
-    c = c < kCells - 1 ? c : kCells - 1;
     const uint2 e = cells[c];
-    const float t = __uint_as_float(e.y) * nrm;
-    const uint32_t idx = e.x + (z > t ? 1u : 0u);
+    const uint32_t idx = e.x + (u > __uint_as_float(e.y) ? 1u : 0u);
     words[r >> 3] = (words[r >> 3] << 4) | idx;
   }
 }

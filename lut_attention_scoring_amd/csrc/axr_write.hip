@@ -100,8 +100,9 @@ void write_kernel(const void* __restrict__ keys, int64_t n, WriteParams prm,
   for (int i = 0; i < 8; ++i) P[i] = prm.tpos[i];
   // 4-bit quantizer's cell table: cell c (position u in [c, c + 1), with
   // u = z cell_k / ||k|| + kCellMid) gets the number of signed thresholds
-  // -tpos[6], ..., -tpos[0], 0, tpos[0], ..., tpos[6] below c and the first
-  // one at or above c (+inf past the last).
+  // -tpos[6], ..., -tpos[0], 0, tpos[0], ..., tpos[6] below c and the
+  // position on the same scale of the first one at or above c (+inf past
+  // the last).
   __shared__ uint2 cells[BITS == 4 ? kCells : 1];
   if constexpr (BITS == 4) {
     for (int c = threadIdx.x; c < kCells; c += kBlock) {
@@ -111,10 +112,11 @@ void write_kernel(const void* __restrict__ keys, int64_t n, WriteParams prm,
 #pragma unroll
       for (int i = 0; i < 15; ++i) {
         const float th = i < 7 ? -P[6 - i] : (i == 7 ? 0.0f : P[i - 8]);
-        if (fmaf(th, prm.cell_k, kCellMid) < static_cast<float>(c)) {
+        const float pos = fmaf(th, prm.cell_k, kCellMid);
+        if (pos < static_cast<float>(c)) {
           ++cnt;
         } else if (!found) {
-          nxt = th;
+          nxt = pos;
           found = true;
         }
       }
@@ -206,7 +208,7 @@ void write_kernel(const void* __restrict__ keys, int64_t n, WriteParams prm,
             (nrm == 0.0f || (nrm >= 0x1p-100f && nrm <= 0x1p100f));
         if (__builtin_amdgcn_ballot_w64(!cells_ok) == 0) {
           const float cells_per_z = nrm > 0.0f ? prm.cell_k / nrm : 0.0f;
-          quantize_cells(x, cells_per_z, nrm, cells, words);
+          quantize_cells(x, cells_per_z, cells, words);
         } else {
           quantize_lane<BITS>(x, S, words);
         }
