@@ -32,6 +32,12 @@ __device__ __forceinline__ float lane_xor(float v) {
   return __uint_as_float(lane_xor_u32<M>(__float_as_uint(v)));
 }
 
+// Value held by lane (lane ^ 7) inside each group of 8 lanes: DPP
+// row_half_mirror.
+__device__ __forceinline__ float lane_mirror8(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+}
+
 // a * b rounded to fp32 on its own: never fused into a later add, so that
 // the softmax partials and the row normalisation see the same scaled score
 // (with a fused multiply-add in one place and a rounded product in the

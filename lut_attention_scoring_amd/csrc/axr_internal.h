@@ -40,7 +40,7 @@ struct WriteParams {
   // (left, right) unit quaternion of each block of 4 coordinates.
   const float* quats;
   // Cells per unit of z / ||k|| of the 4-bit quantizer's cell table (see
-  // the write kernel); 0 for other bit widths.
+  // the write kernel); 0 for other bit widths, or where no scale fits.
   float cell_k;
 };
 

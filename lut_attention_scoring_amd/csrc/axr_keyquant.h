@@ -1,8 +1,9 @@
 // Per-lane write-path arithmetic shared by the kernels that quantize keys:
 // the write kernel, and the score kernel when it appends the new key of a
 // decode step.  A key of d coordinates is held by LPK = d/32 adjacent lanes
-// of a wave (lane u owns coordinates [32u, 32u + 32)); every lane of the
-// wave must be active, since the transform exchanges values across lanes.
+// of a wave (lane u owns the 32 coordinates of block lane_block(u), see
+// below); every lane of the wave must be active, since the transform
+// exchanges values across lanes.
 //
 // "AXELRAM: Quantize Once, Never Dequantize" (arXiv 2604.02638), Abstract:
 // the seeded sign pattern and normalised Walsh-Hadamard transform make each
@@ -21,12 +22,27 @@ namespace axr {
 typedef _Float16 half2_v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 
-// One butterfly stage across lanes at distance M (see the file comment):
-// x <- x + m * x[lane ^ M].  Distances 1, 2 and 8 are single v_fmac_f32 with a
-// DPP source operand; each block of 16 starts with s_nop 1 because a DPP read
-// of a VGPR needs two wait states after the VALU write of that VGPR, and the
-// instructions of a block read and write disjoint registers.  Distance 4 has
-// no DPP pattern and goes through ds_swizzle.
+// The block of 32 coordinates that lane u of a key holds.  The lane stages
+// of the transform pair lanes u and u ^ M for the masks M = 1, 2, 7, 8 (the
+// ones DPP reaches: quad permutations, the mirror inside 8 lanes, and a
+// rotation by 8 inside 16; lane xor 4 has no DPP pattern).  Over the basis
+// 1, 2, 7, 8 of the lane index, these stages are the butterflies of the
+// 16-point Hadamard transform on the basis coordinates, which are the bits
+// of b(u) = u ^ (3 if bit 2 of u is set): b is linear and maps the masks to
+// 1, 2, 4, 8.  So lane u loads block b(u), its multipliers and sign-pattern
+// bits follow the bits of b(u), and it ends with block b(u) of the output.
+// With at most 4 lanes per key only masks 1 and 2 occur and b(u) = u.
+template <int LPK>
+__device__ __forceinline__ int lane_block(int u) {
+  return LPK >= 8 ? (u ^ ((u & 4) ? 3 : 0)) : u;
+}
+
+// One butterfly stage across lanes with lane mask M (7 standing for the
+// mirror inside 8 lanes, see lane_block): x <- x + m * x[lane ^ M].  Each is
+// a single v_fmac_f32 with a DPP source operand; each block of 16 starts
+// with s_nop 1 because a DPP read of a VGPR needs two wait states after the
+// VALU write of that VGPR, and the instructions of a block read and write
+// disjoint registers.
 #define AXR_FMAC16(CTRL)                                                              \
   asm("s_nop 1\n\t"                                                                  \
       "v_fmac_f32_dpp %0, %0, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
@@ -53,20 +69,17 @@ typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 
 template <int M>
 __device__ __forceinline__ void lane_stage(float (&x)[32], float m) {
-  if constexpr (M == 4) {
 #pragma unroll
-    for (int r = 0; r < 32; ++r) x[r] = fmaf(lane_xor<4>(x[r]), m, x[r]);
-  } else {
-#pragma unroll
-    for (int o = 0; o < 32; o += 16) {
-      if constexpr (M == 1) {
-        AXR_FMAC16("quad_perm:[1,0,3,2]");
-      } else if constexpr (M == 2) {
-        AXR_FMAC16("quad_perm:[2,3,0,1]");
-      } else {
-        static_assert(M == 8, "lane distance must be 1, 2, 4 or 8");
-        AXR_FMAC16("row_ror:8");
-      }
+  for (int o = 0; o < 32; o += 16) {
+    if constexpr (M == 1) {
+      AXR_FMAC16("quad_perm:[1,0,3,2]");
+    } else if constexpr (M == 2) {
+      AXR_FMAC16("quad_perm:[2,3,0,1]");
+    } else if constexpr (M == 7) {
+      AXR_FMAC16("row_half_mirror");
+    } else {
+      static_assert(M == 8, "lane mask must be 1, 2, 7 or 8");
+      AXR_FMAC16("row_ror:8");
     }
   }
 }
@@ -126,18 +139,27 @@ __device__ __forceinline__ uint32_t append_bit(uint32_t w, uint64_t m) {
   return r;
 }
 
+// a + b + (this lane's bit of m), one add whose carry-in is the lane mask.
+__device__ __forceinline__ uint32_t add_with_carry(uint32_t a, uint32_t b, uint64_t m) {
+  uint32_t r;
+  uint64_t carry_out;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %3, %4" : "=v"(r), "=s"(carry_out) : "v"(a), "v"(b), "s"(m));
+  return r;
+}
+
 // 32-bit words of one lane's 32 raw coordinates.
 template <int DT>
 struct RawWords {
   static constexpr int kWords = DT == AXR_F32 ? 32 : 16;
 };
 
-// ||k||: the sum of squares of a lane's coordinates added over the key's lanes.
+// ||k||: the sum of squares of a lane's coordinates added over the key's
+// lanes (partners at lane masks 1, 2, 7, 8, which span every lane of the key).
 template <int LPK>
 __device__ __forceinline__ float key_norm(float ss) {
   if constexpr (LPK >= 2) ss += lane_xor<1>(ss);
   if constexpr (LPK >= 4) ss += lane_xor<2>(ss);
-  if constexpr (LPK >= 8) ss += lane_xor<4>(ss);
+  if constexpr (LPK >= 8) ss += lane_mirror8(ss);
   if constexpr (LPK >= 16) ss += lane_xor<8>(ss);
   return sqrtf(ss);
 }
@@ -163,67 +185,113 @@ __device__ __forceinline__ float rescued_key_norm(float nrm, const float (&x)[32
   return (key_norm<LPK>(ss) * (tiny ? 0x1p-64f : 0x1p64f)) * inv_sqrt_d;
 }
 
-// The sign pattern and the Walsh-Hadamard transform for lane u of a key.
-// transform() leaves z = H (s * k) (no 1/sqrt(d)) in x and returns ||k||.
+// First butterfly stage of raw words o .. o + 3 (fp16 or bf16 pairs): x[2i]
+// and x[2i + 1] are the dot products of raw[i] with sg[i] and with sg[i]
+// negated in its high half.  A VALU read or write of a dot product's result
+// needs three wait states after it on this architecture, which the compiler
+// does not insert for inline asm: the trailing s_nop 2 provides them.
+#define AXR_DOT2X8(OP)                                                              \
+  asm(OP " %0, %8, %12, 0\n\t" OP " %1, %8, %12, 0 neg_hi:[0,1,0]\n\t"                \
+      OP " %2, %9, %13, 0\n\t" OP " %3, %9, %13, 0 neg_hi:[0,1,0]\n\t"                \
+      OP " %4, %10, %14, 0\n\t" OP " %5, %10, %14, 0 neg_hi:[0,1,0]\n\t"              \
+      OP " %6, %11, %15, 0\n\t" OP " %7, %11, %15, 0 neg_hi:[0,1,0]\n\t"              \
+      "s_nop 2"                                                                     \
+      : "=&v"(x[2 * o]), "=&v"(x[2 * o + 1]), "=&v"(x[2 * o + 2]), "=&v"(x[2 * o + 3]), \
+        "=&v"(x[2 * o + 4]), "=&v"(x[2 * o + 5]), "=&v"(x[2 * o + 6]), "=&v"(x[2 * o + 7]) \
+      : "v"(raw[o]), "v"(raw[o + 1]), "v"(raw[o + 2]), "v"(raw[o + 3]), "v"(sg[o]),    \
+        "v"(sg[o + 1]), "v"(sg[o + 2]), "v"(sg[o + 3]))
+
+// The sign pattern and the Walsh-Hadamard transform for one lane of a key,
+// the lane holding coordinate block blk = lane_block(u).  transform() leaves
+// z = H (s * k) (no 1/sqrt(d)) in x and returns ||k||.
 template <int D, int DT>
 struct WhtLane {
   static constexpr int LPK = D / 32;
   static constexpr int NW = RawWords<DT>::kWords;
-  uint32_t xm[NW];
-  float m1, m2, m4, m8;
+  static constexpr bool kDotStage = DT != AXR_F32 && LPK >= 8;
+  // fp16 / bf16: per raw word, the pair (+-1, +-1) in the key's format that
+  // multiplies its two coordinates (only its sign bits without the dot
+  // product stage); fp32: the sign bit to xor into each coordinate
+  uint32_t sg[NW];
+  float m1, m2, m7, m8;
 
-  // Per-lane xor masks on the raw words: the sign pattern of this lane's 32
-  // coordinates, plus a flip of everything when popcount(u) is odd (which
-  // makes every lane stage a single fused multiply-add).
-  __device__ __forceinline__ void init(const uint32_t* sign_words, int u) {
-    const uint32_t sw = sign_words[u] ^ ((__popc(u) & 1) ? 0xFFFFFFFFu : 0u);
+  // The sign pattern of the block's 32 coordinates, times -1 throughout
+  // when popcount(blk) is odd (which makes every lane stage a single fused
+  // multiply-add), and the lane-stage multipliers from the bits of blk.
+  __device__ __forceinline__ void init(const uint32_t* sign_words, int blk) {
+    const uint32_t sw = sign_words[blk] ^ ((__popc(blk) & 1) ? 0xFFFFFFFFu : 0u);
+    constexpr uint32_t one = DT == AXR_F16 ? 0x3C00u : 0x3F80u;   // 1.0 in the half format
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       if constexpr (DT == AXR_F32) {
-        xm[i] = ((sw >> i) & 1u) << 31;
+        sg[i] = ((sw >> i) & 1u) << 31;
       } else {
-        xm[i] = (((sw >> (2 * i)) & 1u) << 15) | (((sw >> (2 * i + 1)) & 1u) << 31);
+        sg[i] = ((((sw >> (2 * i)) & 1u) << 15) | (((sw >> (2 * i + 1)) & 1u) << 31)) |
+                (kDotStage ? one * 0x10001u : 0u);
       }
     }
-    m1 = (u & 1) ? 1.0f : -1.0f;
-    m2 = (u & 2) ? 1.0f : -1.0f;
-    m4 = (u & 4) ? 1.0f : -1.0f;
-    m8 = (u & 8) ? 1.0f : -1.0f;
+    m1 = (blk & 1) ? 1.0f : -1.0f;
+    m2 = (blk & 2) ? 1.0f : -1.0f;
+    m7 = (blk & 4) ? 1.0f : -1.0f;
+    m8 = (blk & 8) ? 1.0f : -1.0f;
   }
 
   __device__ __forceinline__ float transform(const uint32_t (&raw)[NW], float (&x)[32]) const {
-    // sum of squares (sign-independent), first butterfly stage fused with
-    // the conversion to fp32
+    // Sum of squares (sign-independent), and the first butterfly stage
+    // fused with the sign pattern and the conversion to fp32.  For the
+    // half formats with d >= 256 that stage is a dot product of the raw
+    // word with its signs, (lo, hi) . (s0, s1) and (lo, hi) . (s0, -s1) (the
+    // second through the instruction's negate-high modifier): two
+    // instructions per word instead of four.  The products are exact; the
+    // hardware's sum is within 1 ulp of the larger term (not always the
+    // nearest fp32 value; exact when a term is zero), and a sum of two zeros
+    // may come out as +0 where fp32 addition gives -0, which takes the same
+    // index.  At d = 128 the sign flip, conversion and add / subtract
+    // measured faster (the dot products' wait states sit on a shorter loop).
     float ss = 0.0f;
-    if constexpr (DT == AXR_F16) {
+    if constexpr (DT == AXR_F16 || DT == AXR_BF16) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint32_t r = raw[i];
-        const half2_v h2 = __builtin_bit_cast(half2_v, r);
-        ss = __builtin_amdgcn_fdot2(h2, h2, ss, false);
-        const uint32_t f = r ^ xm[i];
-        // first butterfly straight from the two fp16 halves: lo + hi, lo - hi
-        asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]"
-            : "=v"(x[2 * i]) : "v"(f));
-        asm("v_fma_mix_f32 %0, %1, -1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]"
-            : "=v"(x[2 * i + 1]) : "v"(f));
+        if constexpr (DT == AXR_F16) {
+          const half2_v h2 = __builtin_bit_cast(half2_v, raw[i]);
+          ss = __builtin_amdgcn_fdot2(h2, h2, ss, false);
+        } else {
+          const bf16x2_v b2 = __builtin_bit_cast(bf16x2_v, raw[i]);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(b2, b2, ss, false);
+        }
       }
-    } else if constexpr (DT == AXR_BF16) {
+      if constexpr (kDotStage) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const bf16x2_v b2 = __builtin_bit_cast(bf16x2_v, raw[i]);
-        ss = __builtin_amdgcn_fdot2_f32_bf16(b2, b2, ss, false);
-        const uint32_t f = raw[i] ^ xm[i];
-        const float lo = __uint_as_float(f << 16);
-        const float hi = __uint_as_float(f & 0xFFFF0000u);
-        x[2 * i] = lo + hi;
-        x[2 * i + 1] = lo - hi;
+        for (int o = 0; o < 16; o += 4) {
+          if constexpr (DT == AXR_F16) {
+            AXR_DOT2X8("v_dot2_f32_f16");
+          } else {
+            AXR_DOT2X8("v_dot2_f32_bf16");
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t f = raw[i] ^ sg[i];
+          if constexpr (DT == AXR_F16) {
+            // lo + hi, lo - hi straight from the two fp16 halves
+            asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]"
+                : "=v"(x[2 * i]) : "v"(f));
+            asm("v_fma_mix_f32 %0, %1, -1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]"
+                : "=v"(x[2 * i + 1]) : "v"(f));
+          } else {
+            const float lo = __uint_as_float(f << 16);
+            const float hi = __uint_as_float(f & 0xFFFF0000u);
+            x[2 * i] = lo + hi;
+            x[2 * i + 1] = lo - hi;
+          }
+        }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float lo = __uint_as_float(raw[2 * i] ^ xm[2 * i]);
-        const float hi = __uint_as_float(raw[2 * i + 1] ^ xm[2 * i + 1]);
+        const float lo = __uint_as_float(raw[2 * i] ^ sg[2 * i]);
+        const float hi = __uint_as_float(raw[2 * i + 1] ^ sg[2 * i + 1]);
         ss = fmaf(lo, lo, ss);
         ss = fmaf(hi, hi, ss);
         x[2 * i] = lo + hi;
@@ -237,11 +305,12 @@ struct WhtLane {
     reg_stage<16>(x);
     if constexpr (LPK >= 2) lane_stage<1>(x, m1);
     if constexpr (LPK >= 4) lane_stage<2>(x, m2);
-    if constexpr (LPK >= 8) lane_stage<4>(x, m4);
+    if constexpr (LPK >= 8) lane_stage<7>(x, m7);
     if constexpr (LPK >= 16) lane_stage<8>(x, m8);
     return nrm;
   }
 };
+#undef AXR_DOT2X8
 
 // The b record words of a lane's 32 coordinates x against the positive
 // thresholds S (already multiplied by the key's scale), filled most
@@ -274,7 +343,9 @@ __device__ __forceinline__ void quantize_lane(const float (&x)[32], const float 
 // cells short of the table's ends for every key whose norm lies in the
 // table's range (the only keys that get here), and a non-finite u converts
 // to 0, so c needs no clamp.  Indices fill the record words a nibble at a
-// time, highest coordinate first.
+// time, highest coordinate first, each appended in one add with carry-in:
+// (w << 4) + cnt + (u > un).  (At b = 3 the threshold search measured as
+// fast: three compares and a select against six VALU slots here.)
 __device__ __forceinline__ void quantize_cells(const float (&x)[32], float kc,
                                                const uint2* cells, uint32_t (&words)[4]) {
 #pragma unroll
@@ -285,8 +356,8 @@ __device__ __forceinline__ void quantize_cells(const float (&x)[32], float kc,
     uint32_t c;
     asm("v_cvt_u32_f32 %0, %1" : "=v"(c) : "v"(u));   // saturating: < 0 -> 0
     const uint2 e = cells[c];
-    const uint32_t idx = e.x + (u > __uint_as_float(e.y) ? 1u : 0u);
-    words[r >> 3] = (words[r >> 3] << 4) | idx;
+    words[r >> 3] = add_with_carry(words[r >> 3] << 4, e.x,
+                                   __builtin_amdgcn_ballot_w64(u > __uint_as_float(e.y)));
   }
 }
 

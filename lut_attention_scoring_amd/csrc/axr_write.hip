@@ -7,16 +7,18 @@
 // indices are stored once and never dequantized.
 //
 // Layout: a key of d coordinates is held by LPK = d/32 adjacent lanes, lane u
-// owning coordinates [32u, 32u + 32) in registers.  The transform is five
-// butterfly stages inside each lane and log2(LPK) stages across lanes.  The
-// 32 indices of a lane are exactly b words of the packed record, so every
-// lane stores its own words and a wave writes one contiguous span.
+// owning the 32 coordinates of block blk = lane_block(u) in registers (blk =
+// u up to d = 128; beyond, a fixed permutation of the blocks that lets every
+// lane stage use DPP).  The transform is five butterfly stages inside each
+// lane and log2(LPK) stages across lanes.  The 32 indices of a lane are
+// exactly b words of the packed record, so every lane stores its own words
+// (at block blk) and a wave writes one contiguous span.
 //
 // Lane stages are one fused multiply-add per coordinate, x + m * partner(x):
-// inputs of lanes whose index has an odd number of set bits are negated on
-// load (folded into the sign-pattern flip), which makes m = -1 for the lane
-// with the stage bit clear and m = +1 for its partner and leaves every value
-// un-negated after the last stage.
+// inputs of lanes whose block index has an odd number of set bits are
+// negated on load (folded into the sign-pattern flip), which makes m = -1
+// for the lane with the stage's bit of blk clear and m = +1 for its partner
+// and leaves every value un-negated after the last stage.
 //
 // Quantization compares z = H(s*k) (before the 1/(sqrt(d)||k||) scale)
 // against thresholds multiplied by sqrt(d)||k||.  For b = 2 and 3: binary
@@ -93,8 +95,10 @@ void write_kernel(const void* __restrict__ keys, int64_t n, WriteParams prm,
   constexpr int NW = RawWords<DT>::kWords;
   const int u = threadIdx.x % LPK;
   const int key_in_block = threadIdx.x / LPK;
+  // the block of the key this lane loads, transforms and stores
+  const int blk = TF == kWht ? lane_block<LPK>(u) : u;
   WhtLane<D, DT> wht;
-  if constexpr (TF == kWht) wht.init(prm.sign, u);
+  if constexpr (TF == kWht) wht.init(prm.sign, blk);
   float P[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) P[i] = prm.tpos[i];
@@ -143,7 +147,7 @@ void write_kernel(const void* __restrict__ keys, int64_t n, WriteParams prm,
     const int64_t key = base + key_in_block;
     const bool valid = key < n;
     const int64_t kc = valid ? key : n - 1;
-    const size_t off = static_cast<size_t>(kc) * D + static_cast<size_t>(u) * 32;
+    const size_t off = static_cast<size_t>(kc) * D + static_cast<size_t>(blk) * 32;
 
     uint32_t raw[NW];
     {
@@ -224,7 +228,7 @@ void write_kernel(const void* __restrict__ keys, int64_t n, WriteParams prm,
         row = key * prm.t_cap + slot;
       }
       if (store) {
-        uint32_t* dst = packed + static_cast<size_t>(row) * W + u * BITS;
+        uint32_t* dst = packed + static_cast<size_t>(row) * W + blk * BITS;
         if constexpr (BITS == 2) {
           *reinterpret_cast<uint2*>(dst) = make_uint2(words[0], words[1]);
         } else if constexpr (BITS == 4) {
@@ -240,7 +244,7 @@ void write_kernel(const void* __restrict__ keys, int64_t n, WriteParams prm,
       if (mode == kWriteTransformNormalized) scale = nrm > 0.0f ? prm.inv_sqrt_d / nrm : 0.0f;
       if (valid) {
         float4* dst = reinterpret_cast<float4*>(yout + static_cast<size_t>(key) * D +
-                                                static_cast<size_t>(u) * 32);
+                                                static_cast<size_t>(blk) * 32);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           dst[i] = make_float4(x[4 * i] * scale, x[4 * i + 1] * scale, x[4 * i + 2] * scale,

@@ -3,7 +3,9 @@
 Indices: bit-exact except coordinates whose oracle value (unit-normalised key,
 after the transform) lies within 1e-6 of a codebook threshold; those may land
 in the neighbouring cell, and there may be at most 1e-4 of all coordinates of
-them.  Scores: given the GPU's own indices, within 1e-5 of
+them, or 2 where that is fewer (the share of coordinates inside the window is
+itself ~1e-4 at b = 3, so on a sample of a few thousand coordinates the
+fraction alone would forbid a single legitimate flip).  Scores: given the GPU's own indices, within 1e-5 of
 ||k|| * sum_j |LUT[j][idx_j]| (the scale of any summation order's rounding).
 Transform: within 1e-5 absolute on unit keys, 1e-5 * ||q|| on queries.
 """
@@ -15,6 +17,7 @@ from oracle import axelram as A
 
 BOUNDARY_WINDOW = 1e-6
 MAX_MISMATCH_FRACTION = 1e-4
+MIN_MISMATCH_ALLOWANCE = 2
 SCORE_RTOL = 1e-5
 TRANSFORM_ATOL = 1e-5
 NORM_RTOL = 1e-5
@@ -40,7 +43,8 @@ def assert_indices(gpu_idx, ora_idx, ora_y, thresholds, label=""):
         assert float(dist.max()) < BOUNDARY_WINDOW, \
             f"{label}: index mismatch {dist.max():.3e} away from any threshold"
         assert np.all(np.abs(gpu_idx[bad] - ora_idx[bad]) == 1), f"{label}: non-adjacent cell"
-    assert nbad <= MAX_MISMATCH_FRACTION * total, f"{label}: {nbad} of {total} indices differ"
+    assert nbad <= max(MAX_MISMATCH_FRACTION * total, MIN_MISMATCH_ALLOWANCE), \
+        f"{label}: {nbad} of {total} indices differ"
     return nbad, total
 
 

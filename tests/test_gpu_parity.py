@@ -267,15 +267,17 @@ def test_tiny_and_huge_keys(scale, dtype, d, b):
     _score_and_check(q, keys, packed, norms, bits, b, label)
 
 
+@pytest.mark.parametrize("b", [3, 4])
 @pytest.mark.parametrize("d", [128, 256, 512])
-def test_b4_threshold_and_cell_sweep(d):
-    """4-bit quantizer: unit keys built so that their transformed
-    coordinates are chosen values (k = s * (H v) gives y = v for a unit v):
+def test_threshold_and_cell_sweep(d, b):
+    """3-bit (threshold search) and 4-bit (cell table) quantizers: unit keys
+    built so that their transformed coordinates are chosen values
+    (k = s * (H v) gives y = v for a unit v):
     a dense sweep over +-3.2 sigma (every cell of the table in that range, a
     few hundred points per cell), points at and within 1e-7..1e-3 of every
     threshold on both sides, and basis keys (y = +-1, the table's ends).
     Indices off by one are allowed only inside the boundary window."""
-    b, per_key = 4, 8
+    per_key = 8
     sigma = 1.0 / np.sqrt(d)
     c, t = A.lloyd_max_codebook(d, b)
     targets = list(np.linspace(-3.2 * sigma, 3.2 * sigma, 8192))
@@ -283,7 +285,7 @@ def test_b4_threshold_and_cell_sweep(d):
         for off in (0.0, 1e-7, 3e-7, 1e-6, 2e-6, 1e-5, 1e-4, 1e-3):
             targets += [th + off, th - off]
     targets = np.array(targets)
-    rng = np.random.default_rng(900 + d)
+    rng = np.random.default_rng(900 + d + 7 * b)
     rng.shuffle(targets)
     nkeys = (len(targets) + per_key - 1) // per_key
     v = np.zeros((nkeys + 2 * 4, d))
@@ -310,12 +312,12 @@ def test_b4_threshold_and_cell_sweep(d):
     bad = gidx != oidx
     if bad.any():
         dist = np.min(np.abs(y[bad][:, None] - t[None, :]), axis=1)
-        assert dist.max() < 1e-6, f"d={d}: index off {dist.max():.3e} from any threshold"
+        assert dist.max() < 1e-6, f"d={d} b={b}: index off {dist.max():.3e} from any threshold"
         assert np.all(np.abs(gidx[bad] - oidx[bad]) == 1)
     far = np.min(np.abs(y[..., None] - t), axis=-1) >= 1e-6
     assert far.sum() > 0.9 * far.size
     assert np.array_equal(gidx[far], oidx[far])
-    assert_norms(f64(norms.reshape(-1)), onorm, f"sweep d={d}")
+    assert_norms(f64(norms.reshape(-1)), onorm, f"sweep d={d} b={b}")
 
 
 @pytest.mark.parametrize("d, b, G", [(128, 3, 64), (128, 3, 63), (128, 4, 40), (256, 3, 64),

@@ -48,3 +48,23 @@ def test_planted_probability_error_fails():
     got[1, 5] *= 1.01
     with pytest.raises(AssertionError):
         assert_softmax(got, lse[0], ref, cond, 1.0, ref.shape[1])
+
+
+def test_index_mismatch_cap():
+    """In-window flips: two are allowed on a small array, a third fails; one
+    outside the window always fails."""
+    from tests._parity import assert_indices
+    t = np.array([-0.5, 0.0, 0.5])
+    y = np.linspace(-1.0, 1.0, 1000)
+    y[[10, 20, 30]] = [0.5 + 1e-7, -0.5 - 2e-7, 3e-7]
+    ora = A.quantize(y, t)
+    got = ora.copy()
+    got[[10, 20]] += np.array([-1, 1])
+    assert assert_indices(got, ora, y, t)[0] == 2
+    got[30] -= 1
+    with pytest.raises(AssertionError):
+        assert_indices(got, ora, y, t)
+    far = ora.copy()
+    far[500] += 1
+    with pytest.raises(AssertionError):
+        assert_indices(far, ora, y, t)
