@@ -495,6 +495,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
     constexpr int FSPLIT = NTHREADS / GROUPS < 1 ? 1
                            : (NTHREADS / GROUPS < HALF_NE ? NTHREADS / GROUPS : HALF_NE);
     static_assert(GROUPS % 64 == 0, "a wave's 64 items share their field index");
+    static_assert(HALF_NE % FSPLIT == 0, "every thread of a triple takes as many fields");
     for (int item = tid; item < GROUPS * FSPLIT; item += NTHREADS) {
       const int vv = item % S::NV;
       const int uu = (item / S::NV) % S::LPK;
@@ -514,7 +515,11 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
         qa[i] = qs[g][j];
         qb[i] = P == 2 ? qs[g][j + P - 1] : 0.0f;
       }
-      for (int f = f0; f < HALF_NE; f += FSPLIT) {
+      // a fixed trip count, unrolled: the centroid loads of every field go
+      // out together instead of one scalar load and wait per entry
+#pragma unroll
+      for (int k = 0; k < HALF_NE / FSPLIT; ++k) {
+        const int f = f0 + k * FSPLIT;
         const float ca = prm.centroid[f & (L - 1)];
         const float cb = P == 2 ? prm.centroid[f >> BITS] : 0.0f;
         if constexpr (SG) {
