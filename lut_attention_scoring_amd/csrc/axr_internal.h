@@ -57,6 +57,7 @@ struct ScoreParams {
   int heads_per_block;            // query heads handled by one block
   int head_groups;                // G / heads_per_block
   int tiles;                      // token tiles per row
+  int row_tiles;                  // (batch, KV head) rows times tiles
   int64_t tile_len;               // tokens per tile
   const int32_t* lens;            // optional device [B]: tokens scored per batch row (<= T)
   // Optional split-T softmax partials, [B][Hq][tiles] pairs (m, l): the

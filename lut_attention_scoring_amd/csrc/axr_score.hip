@@ -9,13 +9,17 @@
 // Design (one block = up to 8 query heads of one (batch, KV head) row, one
 // tile of tokens):
 //   * prologue: q' = H (s * q) / sqrt(d) for the block's heads (LDS), a
-//     power-of-two fixed-point scale per head, and a table of int32 group
-//     sums in LDS.  A group is P = 2 adjacent coordinates (a 2b-bit field of
-//     the packed record, so no index reshuffling) or P = 1 when the pair
-//     table would not fit.  One table entry is 16 bytes: the group sum for 4
-//     heads.  Integer accumulation is exact, so the score's only roundings
-//     are the table entries (2^-30 of the head's full scale) and the final
-//     fp32 multiply.
+//     power-of-two fixed-point scale per head, and a table of group sums in
+//     LDS.  A group is P = 2 adjacent coordinates (a 2b-bit field of the
+//     packed record, so no index reshuffling) or P = 1 when the pair table
+//     would not fit.  One table entry is 16 bytes: the group sum for 4
+//     heads.  Entries are int32: each coordinate term q'_j c_k rounded to a
+//     unit of the head's scale, which puts sum_j |q'_j| max_k |c_k| in
+//     [2^30, 2^31) units, and integer accumulation is exact, so the score's
+//     only roundings are those terms and the final fp32 multiply.  The
+//     signed half table of 4-bit pairs at d = 128 (see ScoreShape) keeps
+//     fp32 entries instead, each the sum of its two rounded terms, summed in
+//     fp32.
 //   * loop: a key is read by LPK = d/32 adjacent lanes, lane u owning the
 //     32 coordinates [32u, 32u+32) = b words of the record, so a wave reads
 //     a contiguous span of records.  Each lane looks up its groups (several
@@ -25,7 +29,8 @@
 //   * work split: one block per CU; the block's tile is cut into units of
 //     one wave's keys, handed out by a per-block LDS counter, so the waves
 //     that the SIMD's issue arbitration favours take more units and all
-//     waves of the block finish together.
+//     waves of the block finish together.  The blocks of a row's head
+//     groups, which read the same records, run on one XCD.
 //   * LDS banks: 16-byte reads are conflict-free when the 16 lanes of a
 //     quarter-wave touch 16 different 16-byte columns of a 256-byte row.  The
 //     table puts group v of lane-chunk u in column (v + KPG*u) mod 16 and each
@@ -236,9 +241,23 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   __shared__ float hinv[GB], hinv2[GB];        // 2^-e of each head's scale, as two exact factors
 
   const int tid = threadIdx.x;
-  const int tile = blockIdx.x % prm.tiles;
-  const int hg = (blockIdx.x / prm.tiles) % prm.head_groups;
-  const int row = blockIdx.x / (prm.tiles * prm.head_groups);
+  // Block id -> (row, tile, head group).  With several head groups, the
+  // blocks of one (row, tile) are 8 ids apart: ids are dealt to the 8 XCDs
+  // round-robin, so they run on one XCD and the later reads of the records
+  // they share hit its L2.  Ids past the last (row, tile) have no work.
+  int tile, hg, row;
+  if (prm.head_groups == 1) {
+    tile = blockIdx.x % prm.tiles;
+    hg = 0;
+    row = blockIdx.x / prm.tiles;
+  } else {
+    const int q8 = blockIdx.x / 8;
+    const int rt = (q8 / prm.head_groups) * 8 + blockIdx.x % 8;
+    if (rt >= prm.row_tiles) return;
+    hg = q8 % prm.head_groups;
+    tile = rt % prm.tiles;
+    row = rt / prm.tiles;
+  }
   const int bi = row / prm.Hkv;
   const int kvh = row % prm.Hkv;
   const int h0 = kvh * prm.G + hg * GB;         // first query head of the block
@@ -806,7 +825,7 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
   constexpr int KPB = (NTHREADS / 64) * S::KPW;
   p.heads_per_block = 4 * NT;
   p.head_groups = (p.G + 4 * NT - 1) / (4 * NT);
-  const int64_t rows = static_cast<int64_t>(B) * p.Hkv * p.head_groups;
+  const int64_t rows = static_cast<int64_t>(B) * p.Hkv * p.head_groups;   // block rows
   const int mode = p.knew != nullptr ? kDecode : (p.partials != nullptr ? kLse : kPlain);
   // One block per CU, each with one tile: a second resident block would
   // halve the tile over which the table build is spread, and the loop is
@@ -819,8 +838,12 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
   tiles = (p.T + tile_len - 1) / tile_len;
   p.tiles = static_cast<int>(tiles);
   p.tile_len = tile_len;
-  const int64_t grid = rows * tiles;
+  const int64_t row_tiles = static_cast<int64_t>(B) * p.Hkv * tiles;
+  // head groups of one (row, tile) 8 block ids apart (see the kernel)
+  const int64_t grid = p.head_groups == 1 ? row_tiles
+                                          : (row_tiles + 7) / 8 * 8 * p.head_groups;
   if (grid > 0x7FFFFFFF) return static_cast<int>(hipErrorInvalidValue);
+  p.row_tiles = static_cast<int>(row_tiles);
   if (plan != nullptr) {                        // planning only: report the tiling
     *plan = p;
     return 0;
