@@ -10,13 +10,15 @@ in HBM before timing starts.
 Prints one JSON line:
   * value: keys per second through the timed steps (whole-job throughput);
   * roofline: the score kernel (the kernel the bandwidth target names) with
-    every launch reading its records from HBM (back to back over four copies
-    of the cache, more than twice the Infinity Cache), duration from HIP
-    events on the stream it runs on; roofline_write: the write kernel alike;
+    every launch reading its records from HBM (back to back over eight copies
+    of the cache, four times the Infinity Cache), duration from HIP events on
+    the stream it runs on; roofline_write: the write kernel alike;
   * configs: write and score kernel times on every workload shape (tiny;
     LLaMA decode; all 36 Qwen2.5-3B layers; long context at b = 2, 3, 4; the
     nine write-sweep cells), each kernel cycling over enough buffer copies
-    that its inputs come from HBM;
+    that its inputs come from HBM.  Per-kernel loops run from a captured
+    graph (one pass over the copies, replayed): a launch through the Python
+    binding costs the host ~20-30 us, more than the shorter kernels take;
   * cpu_baseline: the fp64 oracle on bounded samples of every workload, its
     quantize and score rates reported separately.
 
@@ -114,6 +116,50 @@ def launches_ms(torch, stream, fn, reps, warm_ms=WARM_MS):
     return e0.elapsed_time(e1) / reps
 
 
+def graph_ms(torch, stream, fn, calls, reps, warm_ms=WARM_MS):
+    """Average duration of one of `calls` launches of fn captured in a HIP
+    graph, replayed back to back between HIP events: the host takes ~20-30 us
+    per launch through the binding, longer than the shorter kernels run, so
+    host-launched loops would time the host for them.  The graph holds one
+    pass of fn over the rotating copies (`calls` launches); it is replayed
+    untimed for `warm_ms` first (clock settling), then `reps` launches' worth
+    of replays are timed."""
+    dev = torch.device("cuda:0")
+    for _ in range(calls):                      # eager pass: lazy initialisation
+        fn()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for _ in range(calls):
+            fn()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            fn()
+    torch.cuda.synchronize()
+    n = max(1, reps // calls)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gc.collect()
+    gc.disable()
+    try:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warm_ms * 1e-3:
+            graph.replay()
+            torch.cuda.synchronize()
+        graph.replay()
+        e0.record(stream)
+        for _ in range(n):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
+    del graph
+    return e0.elapsed_time(e1) / (n * calls)
+
+
 class Rotor:
     """Calls fn(copy) cycling over buffer copies."""
 
@@ -124,6 +170,11 @@ class Rotor:
         c = self.copies[self.i % len(self.copies)]
         self.i += 1
         self.fn(c)
+
+
+def graph_calls(k):
+    """Launches per captured graph: whole passes over the k copies, >= 16."""
+    return k * max(1, math.ceil(16 / k))
 
 
 def n_copies(bytes_per_copy, min_copies=4, cycle_bytes=1 << 30):
@@ -148,8 +199,11 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the every-workload section")
     ap.add_argument("--profile", choices=["score_rotating", "score_resident", "write",
-                                          "qwen_score", "long_score_b4", "write_sweep"],
-                    help="run only this kernel's timed loop and print its figure")
+                                          "qwen_score", "long_score_b4", "write_sweep",
+                                          "calibrate"],
+                    help="run only this kernel's timed loop and print its figure "
+                         "(calibrate: a 1 GiB read stream and a 1 GiB write stream, "
+                         "the known sizes that scale rocprofv3's FETCH_SIZE and WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -189,7 +243,7 @@ def time_write(torch, axr, stream, keys, bits, b, reps):
     pairs = list(zip(copies, outs))
     rot = Rotor(pairs, lambda c: axr.quantize_keys(c[0], bits, b, packed=c[1][0],
                                                    norms=c[1][1]))
-    ms = launches_ms(torch, stream, rot, max(reps, k) // k * k)
+    ms = graph_ms(torch, stream, rot, graph_calls(k), reps)
     del copies, outs, pairs
     return {"us": ms * 1e3, "keys_per_s": n / (ms * 1e-3), "bytes": per,
             "GB_per_s": per / (ms * 1e6), "frac_hbm": per / (ms * 1e6) / HBM_PEAK_GBS,
@@ -208,7 +262,7 @@ def time_score(torch, axr, stream, q, packed, norms, bits, b, reps, min_copies=4
         (packed.clone(), norms.clone(), torch.empty(B, Hq, T, device=q.device))
         for _ in range(k - 1)]
     rot = Rotor(copies, lambda c: axr.score(q, c[0], c[1], bits, b, out=c[2]))
-    ms = launches_ms(torch, stream, rot, max(reps, k) // k * k)
+    ms = graph_ms(torch, stream, rot, graph_calls(k), reps)
     del copies
     return {"us": ms * 1e3, "keys_per_s": n / (ms * 1e-3),
             "head_scores_per_s": n * (Hq // Hkv) / (ms * 1e-3), "bytes": per,
@@ -224,14 +278,15 @@ def configs_section(torch, axr, W, stream, reps):
     w = W.tiny()
     keys, q = w["keys"].to(dev), w["q"].to(dev)
     packed, norms = axr.quantize_keys(keys, w["sign_bits"], 3)
-    wr = launches_ms(torch, stream, lambda: axr.quantize_keys(keys, w["sign_bits"], 3,
-                                                              packed=packed, norms=norms), reps)
+    wr = graph_ms(torch, stream, lambda: axr.quantize_keys(keys, w["sign_bits"], 3,
+                                                           packed=packed, norms=norms), 16, reps)
     sc = torch.empty(1, 1, 4096, device=dev)
-    sr = launches_ms(torch, stream, lambda: axr.score(q, packed.view(1, 1, 4096, 12),
-                                                      norms.view(1, 1, 4096), w["sign_bits"], 3,
-                                                      out=sc), reps)
+    sr = graph_ms(torch, stream, lambda: axr.score(q, packed.view(1, 1, 4096, 12),
+                                                   norms.view(1, 1, 4096), w["sign_bits"], 3,
+                                                   out=sc), 16, reps)
     out["tiny_d128_b3_n4096"] = {"keys": 4096, "write_us": wr * 1e3, "score_us": sr * 1e3,
-                                 "note": "back to back; 0.2 MiB per launch, latency-bound"}
+                                 "note": "back to back from a graph; 0.2 MiB per launch, "
+                                         "latency-bound"}
     log("configs: tiny done")
 
     # LLaMA-3.1-8B decode cache (the headline workload)
@@ -261,17 +316,14 @@ def configs_section(torch, axr, W, stream, reps):
     ls = [torch.empty(B, Hq, T, device=dev) for _ in range(L)]
     n = B * Hkv * T
 
-    def write_all():
-        for k, (p, nm) in zip(lk, lp):
-            axr.quantize_keys(k, bits, 4, packed=p, norms=nm)
-
-    def score_all():
-        for qq, (p, nm), s in zip(lq, lp, ls):
-            axr.score(qq, p, nm, bits, 4, out=s)
-
+    # one graph holds a pass over the 36 layers
+    write_one = Rotor(list(zip(lk, lp)), lambda c: axr.quantize_keys(
+        c[0], bits, 4, packed=c[1][0], norms=c[1][1]))
+    score_one = Rotor(list(zip(lq, lp, ls)), lambda c: axr.score(
+        c[0], c[1][0], c[1][1], bits, 4, out=c[2]))
     passes = max(2, reps // 4)
-    wms = launches_ms(torch, stream, write_all, passes)
-    sms = launches_ms(torch, stream, score_all, passes)
+    wms = graph_ms(torch, stream, write_one, L, passes * L) * L
+    sms = graph_ms(torch, stream, score_one, L, passes * L) * L
     wb = write_bytes_per_key(d, 4, 2) * n
     sb = score_bytes_per_key(d, 4, Hq // Hkv) * n
     out["qwen25_3b_layer_sweep_d128_b4"] = {
@@ -317,7 +369,7 @@ def time_shaped_stream(torch, axr, stream, in_bytes, out_bytes, reps):
     outs = [torch.empty(out_bytes, dtype=torch.uint8, device=dev) for _ in range(k)]
     rot = Rotor(list(zip(ins, outs)), lambda c: axr.probe_read_write(c[0], in_bytes, c[1],
                                                                     out_bytes))
-    ms = launches_ms(torch, stream, rot, max(reps, k) // k * k)
+    ms = graph_ms(torch, stream, rot, graph_calls(k), reps)
     del ins, outs
     return ms
 
@@ -461,6 +513,22 @@ def main():
 
     if args.profile:
         k = args.profile
+        if k == "calibrate":
+            del keys, q, packed, norms, scores
+            torch.cuda.empty_cache()
+            gib = 1 << 30
+            buf = torch.empty(gib, dtype=torch.uint8, device=dev)
+            sink = torch.zeros(16, dtype=torch.int32, device=dev)
+            buf.fill_(1)
+            torch.cuda.synchronize()
+            rd = launches_ms(torch, stream, lambda: axr.probe_read_stream(buf, sink, gib),
+                             max(args.steps, 3), warm_ms=0.0)
+            wr = launches_ms(torch, stream, lambda: axr.probe_read_write(sink, 0, buf, gib),
+                             max(args.steps, 3), warm_ms=0.0)
+            print(json.dumps({"profile": k, "read_stream_bytes": gib, "read_stream_us": rd * 1e3,
+                              "read_write_stream_write_bytes": gib,
+                              "read_write_stream_us": wr * 1e3}), flush=True)
+            return
         if k == "write_sweep":
             del keys, q, packed, norms, scores
             torch.cuda.empty_cache()
@@ -472,9 +540,9 @@ def main():
                            min_copies=4 if k == "score_rotating" else 1) \
                 if k == "score_rotating" else None
             if r is None:
-                ms = launches_ms(torch, stream,
-                                 lambda: axr.score(q, packed, norms, bits, b, out=scores),
-                                 args.steps)
+                ms = graph_ms(torch, stream,
+                              lambda: axr.score(q, packed, norms, bits, b, out=scores),
+                              16, args.steps)
                 r = {"us": ms * 1e3, "GB_per_s": sbytes / (ms * 1e6)}
         elif k == "write":
             r = time_write(torch, axr, stream, keys, bits, b, args.steps)
@@ -529,11 +597,14 @@ def main():
     def per_launch_ms(fn, reps):
         return launches_ms(torch, stream, fn, reps)
 
+    def per_graph_ms(fn, reps, calls=16):
+        return graph_ms(torch, stream, fn, calls, reps)
+
     log("per-kernel timing")
     write_hbm = time_write(torch, axr, stream, keys, bits, b, args.steps)
     score_hbm = time_score(torch, axr, stream, q, packed, norms, bits, b, args.steps)
-    score_res_ms = per_launch_ms(lambda: axr.score(q, packed, norms, bits, b, out=scores),
-                                 args.steps)
+    score_res_ms = per_graph_ms(lambda: axr.score(q, packed, norms, bits, b, out=scores),
+                                args.steps)
 
     # Decode step on the same cache: one new key per (sequence, KV head)
     # appended at the last slot, then every sequence scored up to it.
@@ -551,9 +622,9 @@ def main():
         append()
         axr.score(q, packed, norms, bits, b, out=scores, lens=lens)
 
-    append_ms = per_launch_ms(append, args.steps)
+    append_ms = per_graph_ms(append, args.steps)
     decode_ms = per_launch_ms(decode_step, args.steps)
-    fused_ms = per_launch_ms(
+    fused_ms = per_graph_ms(
         lambda: axr.decode_step(q, new_k, bits, b, packed, norms, pos, out=scores), args.steps)
     side = torch.cuda.Stream(dev)
     side.wait_stream(stream)
@@ -601,21 +672,21 @@ def main():
     read_ms = per_launch_ms(lambda: axr.probe_read_stream(flush, psink), 10)
     score_in = n * (d * b // 8 + 4)
     score_out = n * 4 * G
-    shaped_ms = per_launch_ms(lambda: axr.probe_read_write(keys, score_in, scores, score_out),
-                              args.steps)
+    shaped_ms = per_graph_ms(lambda: axr.probe_read_write(keys, score_in, scores, score_out),
+                             args.steps)
     kb = keys.view(torch.uint8).reshape(-1)
     nreg = 4
     regions = [(kb[r * score_in:(r + 1) * score_in], torch.empty_like(scores))
                for r in range(min(nreg, kb.numel() // score_in))]
-    rot_stream_ms = per_launch_ms(
+    rot_stream_ms = per_graph_ms(
         Rotor(regions, lambda c: axr.probe_read_write(c[0], score_in, c[1], score_out)),
-        max(args.steps, len(regions)) // len(regions) * len(regions))
+        args.steps, graph_calls(len(regions)))
     del regions, kb
     write_in = n * d * keys.element_size()
     write_out = n * (d * b // 8 + 4)
     wscratch = torch.empty(write_out, dtype=torch.uint8, device=dev)
-    wshaped_ms = per_launch_ms(lambda: axr.probe_read_write(keys, write_in, wscratch, write_out),
-                               args.steps)
+    wshaped_ms = per_graph_ms(lambda: axr.probe_read_write(keys, write_in, wscratch, write_out),
+                              args.steps)
     del flush, sink, wscratch
 
     # Write path with the comparison transforms (block-quaternion rotations)
@@ -634,7 +705,7 @@ def main():
                 ("wht", lambda: axr.quantize_keys(ws_keys, sb, 3, packed=pk, norms=nm)),
                 ("isoquant_full", lambda: axr.quantize_keys_isoquant(ws_keys, qs, 3, True, pk, nm)),
                 ("isoquant_fast", lambda: axr.quantize_keys_isoquant(ws_keys, qs, 3, False, pk, nm))):
-            t_ms = per_launch_ms(fn, args.steps)
+            t_ms = per_graph_ms(fn, args.steps)
             wt[f"d{dd}_{name}"] = {"us": t_ms * 1e3, "GB_per_s": kbytes / (t_ms * 1e6)}
         del ws_keys, pk, nm
 
@@ -714,8 +785,8 @@ def main():
                 "us": score_res_ms * 1e3, "keys_per_s": n / (score_res_ms * 1e-3),
                 "GB_per_s": sbytes / (score_res_ms * 1e6),
                 "frac_of_peak_cache_resident": sbytes / (score_res_ms * 1e6) / HBM_PEAK_GBS,
-                "note": "back to back on one copy: the 136 MiB working set is served from the "
-                        "256 MB Infinity Cache, not HBM"},
+                "note": "back to back on one copy, replayed from a graph: the 136 MiB working "
+                        "set is served from the 256 MB Infinity Cache, not HBM"},
             "score_cold_cache": {"us_median": cold_ms * 1e3, "keys_per_s": n / (cold_ms * 1e-3),
                                  "GB_per_s": sbytes / (cold_ms * 1e6),
                                  "frac_hbm": sbytes / (cold_ms * 1e6) / HBM_PEAK_GBS,
@@ -734,8 +805,10 @@ def main():
             "decode_step": {"us": decode_ms * 1e3, "graph_replay_us": decode_graph_ms * 1e3,
                             "fused_us": fused_ms * 1e3, "append_us": append_ms * 1e3,
                             "appended_keys": B * Hkv, "scored_keys": n,
-                            "note": "append one key per (sequence, KV head) + ragged score; "
-                                    "fused = one launch (axr_decode_step); back to back"},
+                            "note": "append one key per (sequence, KV head) + ragged score, "
+                                    "host-launched back to back (us) and replayed from a "
+                                    "graph; fused = one launch (axr_decode_step) and append "
+                                    "alone, both replayed from a graph"},
         },
         "configs": configs,
     }

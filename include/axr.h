@@ -99,11 +99,18 @@ int axr_quantize_keys(const void* keys, int dtype, int64_t n, int d, int b,
  *   q' = H_d (s * q[bi][h]) / sqrt(d)                 (queries not normalised)
  *   LUT[j][c] = q'_j * centroid_c
  *   scores[bi][h][t] = norms[r] * sum_j LUT[j][idx_j(r)],  r = (bi*Hkv + kvh)*t_cap + t
- * The sum is taken exactly in 32-bit fixed point over table entries that
- * each hold the products of two coordinates (one coordinate at b = 4, whose
- * pair table would not fit in LDS); the only roundings are the table entries
- * (relative 2^-30 of the head's full scale) and the final fp32 products, far
- * inside 1e-5 of norms * sum_j |LUT[j][idx_j]|.
+ * Table entries hold the products of two coordinates (one coordinate where
+ * the pair table would not fit in LDS: b = 4 at d = 256 and 512).  Their sum
+ * is taken exactly in 32-bit fixed point, each coordinate term rounded to a
+ * unit of a per-head scale that puts sum_j |q'_j| max_c |centroid_c| in
+ * [2^30, 2^31) units: the error is at most d/2 units, i.e. at most
+ * (d/2) * 1.0001 * (max|c| / min|c|) / 2^30 of norms * sum_j |LUT[j][idx_j]|
+ * (max|c| / min|c| = 3.34, 8.78, 21.3 for b = 2, 3, 4): 2.0e-7, 5.2e-7 at
+ * d = 128 (b = 2, 3); 4.0e-7, 1.0e-6, 2.5e-6 at d = 256; 8.0e-7, 2.1e-6,
+ * 5.1e-6 at d = 512 (b = 2, 3, 4), plus ~1e-7 for the final fp32 products.
+ * At d = 128, b = 4 the entries are fp32 (the pair table is stored for half
+ * the field values, see the score kernel), summed in fp32: at most ~20 fp32
+ * roundings, ~1.2e-6 of the same scale.  Every case is inside 1e-5.
  *   q       : device, [B][Hq][d] of q_dtype, 16-byte aligned
  *   packed  : device uint32, [B][Hkv][t_cap][W] as written by axr_quantize_keys
  *   norms   : device float, [B][Hkv][t_cap]
