@@ -44,6 +44,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CUS, CLOCK_HZ = 256, 2.4e9        # MI355X compute units and peak engine clock
 METRIC = "quantized keys scored/sec + achieved HBM GB/s (d=128, b=3, GQA decode)"
 CSRC = os.path.join(ROOT, "lut_attention_scoring_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -85,6 +86,28 @@ def counter_traffic(kernel):
                     fk, wk, ff, wf = (float(m.group(i)) for i in range(3, 7))
                     return (fk * ff + wk * wf) * 1024.0
     return None
+
+
+def counter_valu(kernel):
+    """VALU wave instructions per launch from the rocprofv3 SQ_INSTS_VALU pass
+    summarised in profiles/ (a line "counter-valu: kernel=K sources_sha1=S
+    valu_per_launch=V"), gated on the sources' SHA-1 like counter_traffic."""
+    want = sources_sha1(kernel)
+    pat = re.compile(r"counter-valu:\s*kernel=(\w+)\s+sources_sha1=([0-9a-f]+)\s+"
+                     r"valu_per_launch=([0-9.]+)")
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        with open(path) as f:
+            for m in pat.finditer(f.read()):
+                if m.group(1) == kernel and m.group(2) == want:
+                    return float(m.group(3))
+    return None
+
+
+def valu_issue(kernel, us):
+    """Wave64 VALU instructions per CU-cycle over a launch of `us` (256 CUs at
+    2.4 GHz), from the counted instructions; None without a current count."""
+    v = counter_valu(kernel)
+    return None if v is None else round(v / (CUS * CLOCK_HZ * us * 1e-6), 3)
 
 
 def launches_ms(torch, stream, fn, reps, warm_ms=WARM_MS):
@@ -755,14 +778,16 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(score_hbm["GB_per_s"] / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic("score"), "bytes_per_launch": sbytes,
-                     "us": score_hbm["us"]},
+                     "us": score_hbm["us"],
+                     "valu_per_cu_cycle": valu_issue("score", score_hbm["us"])},
         "roofline_write": {"kernel": "write", "source": f"HBM ({write_hbm['copies']} rotating "
                                                         "copies of the keys)",
                            "bound": "hbm", "achieved": round(write_hbm["GB_per_s"], 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(write_hbm["GB_per_s"] / HBM_PEAK_GBS, 4),
                            "traffic": counter_traffic("write"), "bytes_per_launch": wbytes,
-                           "us": write_hbm["us"]},
+                           "us": write_hbm["us"],
+                           "valu_per_cu_cycle": valu_issue("write", write_hbm["us"])},
         "step_kernels": {"write_us": step_write_ms * 1e3, "score_us": step_score_ms * 1e3,
                          "note": "HIP events around each kernel inside the timed steps; the "
                                  "score kernel there reads records the write kernel has just "
