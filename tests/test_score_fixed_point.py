@@ -17,7 +17,10 @@ sums) on the worst-case inputs of tests/_adversarial.py and checks:
 * the integer sums fit int32 for every index pattern.
 
 It models the kernel's design; it is not the oracle (the exact scores come
-from oracle.axelram)."""
+from oracle.axelram).  At d = 128, b = 4 the kernel keeps fp32 entries
+instead (the signed half table of 4-bit pairs, summed in fp32); there the
+integer model below is a bound of a design not in use, and the kernel's own
+arithmetic is checked on the GPU (tests/test_gpu_score_bound.py)."""
 
 import numpy as np
 import pytest
