@@ -144,6 +144,22 @@ static axr::WriteParams write_params(const uint32_t* sign_bits, int d, int b,
   p.inv_sqrt_d = static_cast<float>(1.0 / sqrt_d);
   p.cell_k = b == 4 ? cached_cell_scale(d, b, tf, p.tpos, half, tf == axr::kWht ? sqrt_d : 1.0)
                    : 0.0f;
+  if (p.cell_k > 0.0f) {
+    // positions of the 15 signed thresholds on the cell scale, ascending, in
+    // the fp32 arithmetic the kernel compares with
+    float pos[axr::kMaxLevels - 1];
+    for (int i = 0; i < 15; ++i) {
+      const float th = i < 7 ? -p.tpos[6 - i] : (i == 7 ? 0.0f : p.tpos[i - 8]);
+      pos[i] = std::fmaf(th, p.cell_k, axr::kCellMid);
+    }
+    for (int c = 0; c < axr::kCells; ++c) {
+      uint32_t cnt = 0;
+      while (cnt < 15 && pos[cnt] < static_cast<float>(c)) ++cnt;
+      const float nxt = cnt < 15 ? pos[cnt] : INFINITY;
+      p.cells[2 * c] = cnt;
+      std::memcpy(&p.cells[2 * c + 1], &nxt, 4);
+    }
+  }
   p.t_cap = 0;
   p.Hkv = 1;
   return p;

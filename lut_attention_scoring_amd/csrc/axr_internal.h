@@ -42,6 +42,12 @@ struct WriteParams {
   // Cells per unit of z / ||k|| of the 4-bit quantizer's cell table (see
   // the write kernel); 0 for other bit widths, or where no scale fits.
   float cell_k;
+  // The table itself when cell_k > 0, filled on the host: for cell c,
+  // cells[2c] = the number of signed thresholds -tpos[6], ..., 0, ...,
+  // tpos[6] whose position t cell_k + kCellMid (fp32 fused multiply-add)
+  // lies below c, cells[2c + 1] = the bits of the first such position at or
+  // above c (+inf past the last).
+  uint32_t cells[2 * kCells];
 };
 
 // Write-path transforms: the method's sign pattern + Walsh-Hadamard, and the

@@ -102,30 +102,13 @@ void write_kernel(const void* __restrict__ keys, int64_t n, WriteParams prm,
   float P[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) P[i] = prm.tpos[i];
-  // 4-bit quantizer's cell table: cell c (position u in [c, c + 1), with
-  // u = z cell_k / ||k|| + kCellMid) gets the number of signed thresholds
-  // -tpos[6], ..., -tpos[0], 0, tpos[0], ..., tpos[6] below c and the
-  // position on the same scale of the first one at or above c (+inf past
-  // the last).
+  // 4-bit quantizer's cell table (cell c: position u in [c, c + 1), with
+  // u = z cell_k / ||k|| + kCellMid): the host's table from the kernel
+  // arguments, copied to LDS.
   __shared__ uint2 cells[BITS == 4 ? kCells : 1];
   if constexpr (BITS == 4) {
-    for (int c = threadIdx.x; c < kCells; c += kBlock) {
-      uint32_t cnt = 0u;
-      float nxt = INFINITY;
-      bool found = false;
-#pragma unroll
-      for (int i = 0; i < 15; ++i) {
-        const float th = i < 7 ? -P[6 - i] : (i == 7 ? 0.0f : P[i - 8]);
-        const float pos = fmaf(th, prm.cell_k, kCellMid);
-        if (pos < static_cast<float>(c)) {
-          ++cnt;
-        } else if (!found) {
-          nxt = pos;
-          found = true;
-        }
-      }
-      cells[c] = make_uint2(cnt, __float_as_uint(nxt));
-    }
+    for (int c = threadIdx.x; c < kCells; c += kBlock)
+      cells[c] = make_uint2(prm.cells[2 * c], prm.cells[2 * c + 1]);
     __syncthreads();
   }
   // quaternions of this lane's eight blocks (comparison transform only)
