@@ -200,6 +200,31 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c
   return r;
 }
 
+// ((byte k of w) ^ (byte 0 of m)) << 8, zeros elsewhere: one xor with SDWA
+// byte selects (k is a compile-time constant after unrolling).
+__device__ __forceinline__ uint32_t xor_byte_to_byte1(uint32_t w, uint32_t m, int k) {
+  uint32_t r;
+  switch (k) {
+    case 0:
+      asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PAD src0_sel:BYTE_0 "
+          "src1_sel:BYTE_0" : "=v"(r) : "v"(w), "v"(m));
+      break;
+    case 1:
+      asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PAD src0_sel:BYTE_1 "
+          "src1_sel:BYTE_0" : "=v"(r) : "v"(w), "v"(m));
+      break;
+    case 2:
+      asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PAD src0_sel:BYTE_2 "
+          "src1_sel:BYTE_0" : "=v"(r) : "v"(w), "v"(m));
+      break;
+    default:
+      asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PAD src0_sel:BYTE_3 "
+          "src1_sel:BYTE_0" : "=v"(r) : "v"(w), "v"(m));
+      break;
+  }
+  return r;
+}
+
 template <int WL>
 __device__ __forceinline__ void buffer_load_words(uint32_t (&dst)[WL], __amdgpu_buffer_rsrc_t r,
                                                   uint32_t voff, uint32_t soff) {
@@ -230,7 +255,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
                                                        float* __restrict__ scores,
                                                        ScoreParams prm) {
   using S = ScoreShape<D, BITS, P, SG>;
-  static_assert(!SG || S::LPK == 4, "signed half tables are built for d = 128");
+  static_assert(!SG || (S::LPK == 4 && S::FB == 8),
+                "signed half tables are built for 8-bit pair fields at d = 128");
   constexpr int GB = 4 * NT;                    // heads per block (some may be padding)
   constexpr int L = 1 << BITS;                  // codebook levels
   constexpr int HL = L / 2;
@@ -678,15 +704,20 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
         for (int sc = 0; sc < CH; ++sc) {
 #pragma unroll
           for (int il = 0; il < IL; ++il) {
-            const uint32_t x = field_shl8_raw<S::WL>(w[il], (st0 + sc) * S::FB, S::FB);
             uint32_t addr;
             if constexpr (SG) {
-              // m = all ones when the field's top bit (bit 8 + FB - 1 of x) is
-              // set: the entry of the mirrored field ~f, negated
-              const int32_t m = static_cast<int32_t>(x << (24 - S::FB)) >> 31;
-              addr = and_or(x ^ static_cast<uint32_t>(m), fmask, boff[st0 + sc]);
+              // field f = byte k of record word i; m = all ones when its top
+              // bit is set: the entry of the mirrored field ~f, negated, at
+              // ((f ^ m) & 0xFF) << 8 (the top bit then clear) past the
+              // lane's step offset
+              const int pos = (st0 + sc) * S::FB;
+              const uint32_t wd = w[il][pos >> 5];
+              const int k = (pos & 31) >> 3;
+              const int32_t m = static_cast<int32_t>(wd << (24 - 8 * k)) >> 31;
+              addr = xor_byte_to_byte1(wd, static_cast<uint32_t>(m), k) + boff[st0 + sc];
               sg[sc][il] = __uint_as_float((static_cast<uint32_t>(m) & 0x80000000u) | 0x3F800000u);
             } else {
+              const uint32_t x = field_shl8_raw<S::WL>(w[il], (st0 + sc) * S::FB, S::FB);
               addr = and_or(x, fmask, boff[st0 + sc]);
             }
 #pragma unroll
