@@ -589,8 +589,9 @@ def main():
 
     # Steps run untimed for settle_ms first: a write + score loop starting
     # from an idle chip runs its first ~10 ms up to half slower while the
-    # clock ramps; then the warmup steps, then the timed steps with HIP events
-    # around each kernel (on the stream the kernels run on).
+    # clock ramps; then the warmup steps, then the timed steps (wall clock
+    # between two synchronisations), then as many steps with HIP events
+    # around each kernel (on the stream the kernels run on) for the split.
     log(f"settle {args.settle_ms:.0f} ms, warmup {args.warmup}, timing {args.steps} steps")
     gc.collect()
     gc.disable()
@@ -601,9 +602,16 @@ def main():
         torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # The same number of steps again with HIP events around each kernel, for
+    # the split between the two: an event recorded between the kernels costs
+    # the GPU ~2 us, so these are not the timed steps.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for e in ev:
         e[0].record(stream)
         axr.quantize_keys(keys, bits, b, packed=packed, norms=norms)
@@ -611,7 +619,6 @@ def main():
         axr.score(q, packed, norms, bits, b, out=scores)
         e[2].record(stream)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     gc.enable()
     ms_per_step = elapsed * 1e3 / args.steps
     step_write_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
@@ -789,9 +796,11 @@ def main():
                            "us": write_hbm["us"],
                            "valu_per_cu_cycle": valu_issue("write", write_hbm["us"])},
         "step_kernels": {"write_us": step_write_ms * 1e3, "score_us": step_score_ms * 1e3,
-                         "note": "HIP events around each kernel inside the timed steps; the "
-                                 "score kernel there reads records the write kernel has just "
-                                 "written"},
+                         "note": "HIP events around each kernel in a second pass of as many "
+                                 "steps right after the timed ones (events between the "
+                                 "kernels cost GPU time, so they stay out of the timed steps); "
+                                 "the score kernel there reads records the write kernel has "
+                                 "just written"},
         "ceiling": {
             "read_stream_GB_per_s": flush_bytes / (read_ms * 1e-3) / 1e9,
             "read_stream_bytes": flush_bytes,
