@@ -222,7 +222,8 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the every-workload section")
     ap.add_argument("--profile", choices=["score_rotating", "score_resident", "write",
-                                          "qwen_score", "long_score_b4", "write_sweep",
+                                          "qwen_score", "long_score_b2", "long_score_b3",
+                                          "long_score_b4", "write_sweep",
                                           "calibrate"],
                     help="run only this kernel's timed loop and print its figure "
                          "(calibrate: a 1 GiB read stream and a 1 GiB write stream, "
@@ -575,8 +576,8 @@ def main():
                 w = W.qwen_layer(0)
                 bb = 4
             else:
-                w = W.long_context(b=4)
-                bb = 4
+                bb = int(k[-1])                   # long_score_b2 / b3 / b4
+                w = W.long_context(b=bb)
             kk, qq = w["keys"].to(dev), w["q"].to(dev)
             pk, nm = axr.quantize_keys(kk, w["sign_bits"], bb)
             r = time_score(torch, axr, stream, qq, pk, nm, w["sign_bits"], bb, args.steps)

@@ -99,8 +99,9 @@ int axr_quantize_keys(const void* keys, int dtype, int64_t n, int d, int b,
  *   q' = H_d (s * q[bi][h]) / sqrt(d)                 (queries not normalised)
  *   LUT[j][c] = q'_j * centroid_c
  *   scores[bi][h][t] = norms[r] * sum_j LUT[j][idx_j(r)],  r = (bi*Hkv + kvh)*t_cap + t
- * Table entries hold the products of two coordinates (one coordinate where
- * the pair table would not fit in LDS: b = 4 at d = 256 and 512).  Their sum
+ * Table entries hold the summed products of a group of coordinates: two
+ * (four for b = 2 at d = 128; one where the pair table would not fit in
+ * LDS: b = 4 at d = 256 and 512).  Their sum
  * is taken exactly in 32-bit fixed point, each coordinate term rounded to a
  * unit of a per-head scale that puts sum_j |q'_j| max_c |centroid_c| in
  * [2^30, 2^31) units: the error is at most d/2 units, i.e. at most

@@ -11,9 +11,9 @@
 //   * prologue: q' = H (s * q) / sqrt(d) for the block's heads (LDS), a
 //     power-of-two fixed-point scale per head, and a table of group sums in
 //     LDS.  A group is P = 2 adjacent coordinates (a 2b-bit field of the
-//     packed record, so no index reshuffling) or P = 1 when the pair table
-//     would not fit.  One table entry is 16 bytes: the group sum for 4
-//     heads.  Entries are int32: each coordinate term q'_j c_k rounded to a
+//     packed record, so no index reshuffling), P = 4 for 2-bit indices at
+//     d = 128 (8-bit fields), or P = 1 when the pair table would not fit.
+//     One table entry is 16 bytes: the group sum for 4 heads.  Entries are int32: each coordinate term q'_j c_k rounded to a
 //     unit of the head's scale, which puts sum_j |q'_j| max_k |c_k| in
 //     [2^30, 2^31) units, and integer accumulation is exact, so the score's
 //     only roundings are those terms and the final fp32 multiply.  The
@@ -172,8 +172,16 @@ struct ScoreShape {
   static constexpr int NE = 1 << FB;            // field values per group
   static constexpr int NES = SG ? NE / 2 : NE;  // entries stored per group
   static constexpr int NV = 32 / P;             // groups per lane
-  static constexpr int ROWS_U = (NV / 16) * NES;  // 256-byte rows per lane chunk
-  static constexpr int TBYTES = 256 * LPK * ROWS_U;  // bytes per 4-head table
+  // Sets of NES 256-byte rows: one per 16 groups of a lane chunk.  With
+  // fewer than 16 groups per chunk (P = 4), chunk u's groups take the
+  // columns (v + KPG u) mod 16, v < NV, and the chunks u, u + RS, ... take
+  // disjoint columns, so they share one row set.
+  static constexpr int RS = LPK * NV / 16;      // row sets per 4-head table
+  static constexpr int TBYTES = 256 * NES * RS;  // bytes per 4-head table
+  // first row of the set holding group v of chunk u
+  static constexpr int row_base(int u, int v) {
+    return NV >= 16 ? (u * (NV / 16) + v / 16) * NES : (u % RS) * NES;
+  }
 };
 
 constexpr int IL = 1;                // record units processed together
@@ -265,6 +273,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   __shared__ int4 lut[NT * (S::TBYTES / 16)];
   __shared__ float qs[GB][D];
   __shared__ float hinv[GB], hinv2[GB];        // 2^-e of each head's scale, as two exact factors
+  __shared__ int4 qterm[P == 4 ? (1 << BITS) * D : 1];  // rounded terms of a 4-coordinate table
 
   const int tid = threadIdx.x;
   // Block id -> (row, tile, head group).  With several head groups, the
@@ -293,7 +302,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   const int kw = lane / S::LPK;                 // key index in the wave
   constexpr uint32_t REC_BYTES = S::W * 4;
   constexpr int CH = 8 / NT < S::NV ? 8 / NT : S::NV;  // steps per batch of lookups
-  constexpr int PD = NT == 1 ? 3 : 2;           // record units in flight per wave
+  // record units in flight per wave: the 4-coordinate table's units cost
+  // the fewest instructions, so more of them are kept in flight (5 measured
+  // fastest, against 3, 4, 6 and 8)
+  constexpr int PD = NT == 1 ? (P == 4 ? 5 : 3) : 2;
   // tokens [0, len) of this batch row are scored: T, or lens[bi] (clamped),
   // or pos[bi] + 1 in a fused decode step
   int64_t len = prm.T;
@@ -527,10 +539,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   //    field f).  The codebook is symmetric (c[L-1-k] = -c[k]), so the entry
   //    of the fully mirrored field is the negation: each task rounds the
   //    coordinate terms once and writes an entry and its mirror.  A pair
-  //    entry is the sum of its two rounded coordinate terms.
+  //    (or 4-coordinate) entry is the sum of its rounded coordinate terms.
   {
     auto slot_of = [](int uu, int vv, int ff) {
-      return 16 * (uu * S::ROWS_U + (vv / 16) * S::NES + ff) + ((vv + S::KPG * uu) & 15);
+      return 16 * (S::row_base(uu, vv) + ff) + ((vv + S::KPG * uu) & 15);
     };
     constexpr int HALF_NE = S::NE / 2;           // fields with the top bit clear
     constexpr int GROUPS = NT * S::LPK * S::NV;  // (table, chunk, group) triples
@@ -539,6 +551,42 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
     // fastest: the 16 lanes of a quarter-wave write 16 distinct LDS columns.
     constexpr int FSPLIT = NTHREADS / GROUPS < 1 ? 1
                            : (NTHREADS / GROUPS < HALF_NE ? NTHREADS / GROUPS : HALF_NE);
+    static_assert(P != 4 || (BITS == 2 && !SG && NT == 1 && S::LPK == 4),
+                  "4-coordinate groups are built for b = 2 at d = 128, one table");
+    if constexpr (P == 4) {
+      // (a) the rounded coordinate terms q'_j c_k 2^e of the 4 heads, one
+      //     16-byte record per (level k, coordinate c of its group, group g)
+      //     at ((4 k + c) 32 + g), heads already in chunk g / 8's component
+      //     order; (b) each entry the sum of its four terms.  Group index
+      //     fastest in both: the 16 lanes of a quarter-wave read 16 columns.
+      constexpr int NG = D / 4;                  // groups of a key
+      for (int t = tid; t < L * 4 * NG; t += NTHREADS) {
+        const int g = t % NG, c = (t / NG) % 4, k = t / (4 * NG);
+        const int j = 4 * g + c;
+        const int pu = (j / 32) & 3;
+        const float ck = prm.centroid[__builtin_amdgcn_readfirstlane(k)];
+        int e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = __float2int_rn(qs[i ^ pu][j] * ck);
+        qterm[t] = make_int4(e[0], e[1], e[2], e[3]);
+      }
+      __syncthreads();
+      for (int item = tid; item < NG * HALF_NE; item += NTHREADS) {
+        const int g = item % NG, f = item / NG;  // f: top bit clear
+        const int uu = g / S::NV, vv = g % S::NV;
+        int4 e = qterm[(4 * (f & 3) + 0) * NG + g];
+#pragma unroll
+        for (int c = 1; c < 4; ++c) {
+          const int4 t = qterm[(4 * ((f >> (2 * c)) & 3) + c) * NG + g];
+          e.x += t.x;
+          e.y += t.y;
+          e.z += t.z;
+          e.w += t.w;
+        }
+        lut[slot_of(uu, vv, f)] = e;
+        lut[slot_of(uu, vv, (S::NE - 1) ^ f)] = make_int4(-e.x, -e.y, -e.z, -e.w);
+      }
+    } else {
     static_assert(GROUPS % 64 == 0, "a wave's 64 items share their field index");
     static_assert(HALF_NE % FSPLIT == 0, "every thread of a triple takes as many fields");
     for (int item = tid; item < GROUPS * FSPLIT; item += NTHREADS) {
@@ -553,27 +601,29 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
       // u ^ i (see quad_reduce_scatter); otherwise heads are in order.  The
       // coordinates are read in that order, q'_j 2^e (stored scaled).
       const int pu = S::LPK == 4 ? (uu & 3) : 0;
-      float qa[4], qb[4];
+      float qc[P][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int g = 4 * t4 + (i ^ pu);
-        qa[i] = qs[g][j];
-        qb[i] = P == 2 ? qs[g][j + P - 1] : 0.0f;
+#pragma unroll
+        for (int c = 0; c < P; ++c) qc[c][i] = qs[g][j + c];
       }
       // a fixed trip count, unrolled: the centroid loads of every field go
       // out together instead of one scalar load and wait per entry
 #pragma unroll
       for (int k = 0; k < HALF_NE / FSPLIT; ++k) {
         const int f = f0 + k * FSPLIT;
-        const float ca = prm.centroid[f & (L - 1)];
-        const float cb = P == 2 ? prm.centroid[f >> BITS] : 0.0f;
+        float cc[P];                              // centroid of each coordinate's index
+#pragma unroll
+        for (int c = 0; c < P; ++c) cc[c] = prm.centroid[(f >> (BITS * c)) & (L - 1)];
         if constexpr (SG) {
-          // fp32 entry: the two coordinate terms, rounded, then their sum
+          // fp32 entry: the coordinate terms, rounded, then their sum
           float ef[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float ta = mul_rounded(qa[i], ca);
-            ef[i] = P == 2 ? ta + mul_rounded(qb[i], cb) : ta;
+            ef[i] = mul_rounded(qc[0][i], cc[0]);
+#pragma unroll
+            for (int c = 1; c < P; ++c) ef[i] += mul_rounded(qc[c][i], cc[c]);
           }
           tab[slot_of(uu, vv, f)] = make_int4(__float_as_int(ef[0]), __float_as_int(ef[1]),
                                               __float_as_int(ef[2]), __float_as_int(ef[3]));
@@ -582,16 +632,15 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
         int e[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if constexpr (P == 1) {
-            e[i] = __float2int_rn(qa[i] * ca);
-          } else {
-            e[i] = __float2int_rn(qa[i] * ca) + __float2int_rn(qb[i] * cb);
-          }
+          e[i] = __float2int_rn(qc[0][i] * cc[0]);
+#pragma unroll
+          for (int c = 1; c < P; ++c) e[i] += __float2int_rn(qc[c][i] * cc[c]);
         }
         const int fm = (S::NE - 1) ^ f;            // every field mirrored
         tab[slot_of(uu, vv, f)] = make_int4(e[0], e[1], e[2], e[3]);
         tab[slot_of(uu, vv, fm)] = make_int4(-e[0], -e[1], -e[2], -e[3]);
       }
+    }
     }
   }
 
@@ -602,7 +651,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   for (int st = 0; st < S::NV; ++st) {
     const int vv = (st + kslot) % S::NV;
     boff[st] = static_cast<uint32_t>(
-        256 * (u * S::ROWS_U + (vv / 16) * S::NES) + 16 * ((vv + S::KPG * u) & 15));
+        256 * S::row_base(u, vv) + 16 * ((vv + S::KPG * u) & 15));
   }
   const uint32_t rot = static_cast<uint32_t>(kslot * S::FB);
   const uint32_t fmask = static_cast<uint32_t>(S::NES - 1) << 8;
@@ -841,12 +890,18 @@ constexpr bool fits() { return table_bytes<D, BITS, pick_p<D, BITS, NT>()>(NT) <
 template <int D, int BITS>
 constexpr bool signed_pairs() { return D == 128 && BITS == 4; }
 
+// 2-bit indices at d = 128 in groups of four coordinates: 8-bit fields, 256
+// entries per group, 128 KiB for four heads (half the lookups of pairs).
+template <int D, int BITS>
+constexpr bool quad_groups() { return D == 128 && BITS == 2; }
+
 template <int D, int BITS, int NT, bool SG>
 int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms, int B,
               ScoreParams p, float* scores, hipStream_t s, ScoreParams* plan) {
-  constexpr int P = SG ? 2 : pick_p<D, BITS, NT>();
+  constexpr int P = SG ? 2 : (quad_groups<D, BITS>() ? 4 : pick_p<D, BITS, NT>());
   constexpr int tbytes = table_bytes<D, BITS, P, SG>(NT);
-  constexpr int bytes = tbytes + 4 * NT * D * 4 + 2 * 4 * NT * 4;  // + q' + scales
+  constexpr int bytes = tbytes + 4 * NT * D * 4 + 2 * 4 * NT * 4 +  // + q' + scales
+                        (P == 4 ? (1 << BITS) * D * 16 : 0);        // + the rounded terms
   static_assert(tbytes <= kLdsBudget, "table exceeds the LDS budget");
   // 1024-thread blocks, except the single-coordinate two-table case whose
   // registers need 512-thread blocks.
@@ -894,13 +949,15 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
 }
 
 // Eight heads per block when G >= 8 and both tables fit; otherwise four.
-// The signed half table takes four heads per block (a G = 8 row is two
-// blocks, each reading the records).
+// The signed half table and the 4-coordinate table take four heads per
+// block (a G = 8 row is two blocks, each reading the records).
 template <int D, int BITS>
 int launch_b(const void* q, int qdt, const uint32_t* packed, const float* norms, int B,
              const ScoreParams& p, float* scores, hipStream_t s, ScoreParams* plan) {
   if constexpr (signed_pairs<D, BITS>()) {
     return launch_nt<D, BITS, 1, true>(q, qdt, packed, norms, B, p, scores, s, plan);
+  } else if constexpr (quad_groups<D, BITS>()) {
+    return launch_nt<D, BITS, 1, false>(q, qdt, packed, norms, B, p, scores, s, plan);
   } else {
     if constexpr (fits<D, BITS, 2>()) {
       if (p.G >= 8)

@@ -320,8 +320,8 @@ def test_threshold_and_cell_sweep(d, b):
     assert_norms(f64(norms.reshape(-1)), onorm, f"sweep d={d} b={b}")
 
 
-@pytest.mark.parametrize("d, b, G", [(128, 3, 64), (128, 3, 63), (128, 4, 40), (256, 3, 64),
-                                     (512, 2, 33)])
+@pytest.mark.parametrize("d, b, G", [(128, 3, 64), (128, 3, 63), (128, 4, 40), (128, 2, 33),
+                                     (256, 3, 64), (512, 2, 33)])
 def test_score_largest_groups(d, b, G):
     """Group sizes up to the supported 64 query heads per KV head, including
     ones that leave padded head slots in the last head group of a block."""
