@@ -208,29 +208,52 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c
   return r;
 }
 
-// ((byte k of w) ^ (byte 0 of m)) << 8, zeros elsewhere: one xor with SDWA
-// byte selects (k is a compile-time constant after unrolling).
-__device__ __forceinline__ uint32_t xor_byte_to_byte1(uint32_t w, uint32_t m, int k) {
+// Byte k of x written into byte 1 of a, the other bytes of a kept: one
+// v_mov with SDWA selects (k is a compile-time constant after unrolling).
+__device__ __forceinline__ void byte_into_byte1(uint32_t& a, uint32_t x, int k) {
+  switch (k) {
+    case 0:
+      asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0"
+          : "+v"(a) : "v"(x));
+      break;
+    case 1:
+      asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1"
+          : "+v"(a) : "v"(x));
+      break;
+    case 2:
+      asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_2"
+          : "+v"(a) : "v"(x));
+      break;
+    default:
+      asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
+          : "+v"(a) : "v"(x));
+      break;
+  }
+}
+
+// (byte k of s | byte 0 of c) << 24, zeros elsewhere: with s holding only the
+// top bit of each byte and c = 0x3F, the fp32 value +0.5 or -0.5.
+__device__ __forceinline__ float half_sign(uint32_t s, uint32_t c, int k) {
   uint32_t r;
   switch (k) {
     case 0:
-      asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PAD src0_sel:BYTE_0 "
-          "src1_sel:BYTE_0" : "=v"(r) : "v"(w), "v"(m));
+      asm("v_or_b32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PAD src0_sel:BYTE_0 "
+          "src1_sel:BYTE_0" : "=v"(r) : "v"(s), "v"(c));
       break;
     case 1:
-      asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PAD src0_sel:BYTE_1 "
-          "src1_sel:BYTE_0" : "=v"(r) : "v"(w), "v"(m));
+      asm("v_or_b32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PAD src0_sel:BYTE_1 "
+          "src1_sel:BYTE_0" : "=v"(r) : "v"(s), "v"(c));
       break;
     case 2:
-      asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PAD src0_sel:BYTE_2 "
-          "src1_sel:BYTE_0" : "=v"(r) : "v"(w), "v"(m));
+      asm("v_or_b32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PAD src0_sel:BYTE_2 "
+          "src1_sel:BYTE_0" : "=v"(r) : "v"(s), "v"(c));
       break;
     default:
-      asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PAD src0_sel:BYTE_3 "
-          "src1_sel:BYTE_0" : "=v"(r) : "v"(w), "v"(m));
+      asm("v_or_b32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PAD src0_sel:BYTE_3 "
+          "src1_sel:BYTE_0" : "=v"(r) : "v"(s), "v"(c));
       break;
   }
-  return r;
+  return __uint_as_float(r);
 }
 
 template <int WL>
@@ -625,8 +648,11 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 #pragma unroll
             for (int c = 1; c < P; ++c) ef[i] += mul_rounded(qc[c][i], cc[c]);
           }
-          tab[slot_of(uu, vv, f)] = make_int4(__float_as_int(ef[0]), __float_as_int(ef[1]),
-                                              __float_as_int(ef[2]), __float_as_int(ef[3]));
+          // stored doubled (exact, and finite: every centroid at d = 128,
+          // b = 4 is below 1/4 in magnitude): the loop's sign factor is +-0.5
+          tab[slot_of(uu, vv, f)] = make_int4(
+              __float_as_int(2.0f * ef[0]), __float_as_int(2.0f * ef[1]),
+              __float_as_int(2.0f * ef[2]), __float_as_int(2.0f * ef[3]));
           continue;
         }
         int e[4];
@@ -655,6 +681,16 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   }
   const uint32_t rot = static_cast<uint32_t>(kslot * S::FB);
   const uint32_t fmask = static_cast<uint32_t>(S::NES - 1) << 8;
+  // Signed half table: one address register per step, byte 1 rewritten with
+  // each key's field (the step offset's byte 1 is bit 15, chunk u's low bit,
+  // which the field byte carries as umask), and the constant of half_sign.
+  static_assert(!SG || (IL == 1 && S::row_base(1, 0) == 128 && S::NV == 16),
+                "signed half tables: 128 rows per chunk, one unit at a time");
+  uint32_t sgaddr[S::NV];
+#pragma unroll
+  for (int st = 0; st < S::NV; ++st) sgaddr[st] = boff[st];
+  const uint32_t umask = (u & 1) ? 0x80808080u : 0u;
+  const uint32_t c3f = 0x3Fu;
   // Scores of this block's heads through a raw buffer resource (uniform
   // base: the block's first head row); each lane stores head u (and u + 4)
   // at a fixed per-lane offset plus a per-batch scalar offset.
@@ -736,6 +772,25 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
                                                rnrm, vnrm + ks[pd] * (S::KPW * 4u), 0, 0));
         rotate_right<S::WL>(w[il], rot);
       }
+      // Signed half table: per record word, the top bit of each field byte
+      // (s4) and the entry index of each field (x4): f itself when its top
+      // bit is clear, else its mirror ~f, whose top bit is clear.  The byte
+      // masks (s4 << 1) - (s4 >> 7) are 0xFF exactly where s4 has 0x80 (no
+      // carry crosses a byte; the top byte's wraps modulo 2^32).  Lanes of an
+      // odd chunk also set each byte's top bit: it is bit 15 of their table
+      // offset, the byte that the field fills.
+      uint32_t s4[IL][S::WL], x4[IL][S::WL];
+      if constexpr (SG) {
+#pragma unroll
+        for (int il = 0; il < IL; ++il) {
+#pragma unroll
+          for (int i = 0; i < S::WL; ++i) {
+            s4[il][i] = w[il][i] & 0x80808080u;
+            const uint32_t mff = (s4[il][i] << 1) - (s4[il][i] >> 7);
+            x4[il][i] = w[il][i] ^ mff ^ umask;
+          }
+        }
+      }
 
       using Acc = typename std::conditional<SG, float, uint32_t>::type;
       Acc acc[IL][GB];
@@ -748,23 +803,23 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 #pragma unroll
       for (int st0 = 0; st0 < S::NV; st0 += CH) {
         int4 e[CH][IL][NT];
-        float sg[CH][IL];                         // +-1: field read directly or mirrored
+        float sg[CH][IL];                         // +-0.5: field read directly or mirrored
 #pragma unroll
         for (int sc = 0; sc < CH; ++sc) {
 #pragma unroll
           for (int il = 0; il < IL; ++il) {
             uint32_t addr;
             if constexpr (SG) {
-              // field f = byte k of record word i; m = all ones when its top
-              // bit is set: the entry of the mirrored field ~f, negated, at
-              // ((f ^ m) & 0xFF) << 8 (the top bit then clear) past the
-              // lane's step offset
-              const int pos = (st0 + sc) * S::FB;
-              const uint32_t wd = w[il][pos >> 5];
-              const int k = (pos & 31) >> 3;
-              const int32_t m = static_cast<int32_t>(wd << (24 - 8 * k)) >> 31;
-              addr = xor_byte_to_byte1(wd, static_cast<uint32_t>(m), k) + boff[st0 + sc];
-              sg[sc][il] = __uint_as_float((static_cast<uint32_t>(m) & 0x80000000u) | 0x3F800000u);
+              // field f = byte k of record word i: its entry index (x4's
+              // byte) goes into byte 1 of the step's address register, whose
+              // other bytes hold the lane's step offset; a field with the
+              // top bit set reads its mirror's entry times -1 (the entries
+              // are stored doubled, the sign is +-0.5)
+              const int st = st0 + sc;
+              const int i = st >> 2, k = st & 3;
+              byte_into_byte1(sgaddr[st], x4[il][i], k);
+              addr = sgaddr[st];
+              sg[sc][il] = half_sign(s4[il][i], c3f, k);
             } else {
               const uint32_t x = field_shl8_raw<S::WL>(w[il], (st0 + sc) * S::FB, S::FB);
               addr = and_or(x, fmask, boff[st0 + sc]);
