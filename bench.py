@@ -52,7 +52,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 # Sources whose compiled code a kernel's counter figures depend on.
 KERNEL_SOURCES = {
     "write": ["axr_write.hip", "axr_keyquant.h", "axr_device.h", "axr_internal.h"],
-    "score": ["axr_score.hip", "axr_device.h", "axr_internal.h"],
+    "score": ["axr_score.hip", "axr_keyquant.h", "axr_device.h", "axr_internal.h"],
+    "fused": ["axr_score.hip", "axr_keyquant.h", "axr_device.h", "axr_internal.h"],
 }
 
 WARM_MS = 30.0   # time each kernel runs untimed before its timed launches
@@ -223,7 +224,7 @@ def parse():
                     help="skip the every-workload section")
     ap.add_argument("--profile", choices=["score_rotating", "score_resident", "write",
                                           "qwen_score", "long_score_b2", "long_score_b3",
-                                          "long_score_b4", "write_sweep",
+                                          "long_score_b4", "write_sweep", "fused",
                                           "calibrate"],
                     help="run only this kernel's timed loop and print its figure "
                          "(calibrate: a 1 GiB read stream and a 1 GiB write stream, "
@@ -269,6 +270,28 @@ def time_write(torch, axr, stream, keys, bits, b, reps):
                                                    norms=c[1][1]))
     ms = graph_ms(torch, stream, rot, graph_calls(k), reps)
     del copies, outs, pairs
+    return {"us": ms * 1e3, "keys_per_s": n / (ms * 1e-3), "bytes": per,
+            "GB_per_s": per / (ms * 1e6), "frac_hbm": per / (ms * 1e6) / HBM_PEAK_GBS,
+            "copies": k}
+
+
+def time_fused(torch, axr, stream, keys, q, bits, b, reps):
+    """Quantize-and-score over rotating copies of the keys, each with its own
+    records, norms and score rows."""
+    dev = keys.device
+    B, Hkv, T, d = keys.shape
+    Hq = q.shape[1]
+    n = B * Hkv * T
+    per = (write_bytes_per_key(d, b, keys.element_size()) + 4 * (Hq // Hkv)) * n
+    k = n_copies(per, min_copies=2)
+    copies = [(keys if i == 0 else keys.clone(),
+               torch.empty(B, Hkv, T, d * b // 32, dtype=torch.int32, device=dev),
+               torch.empty(B, Hkv, T, dtype=torch.float32, device=dev),
+               torch.empty(B, Hq, T, dtype=torch.float32, device=dev)) for i in range(k)]
+    rot = Rotor(copies, lambda c: axr.quantize_score(c[0], q, bits, b, packed=c[1], norms=c[2],
+                                                     out=c[3]))
+    ms = graph_ms(torch, stream, rot, graph_calls(k), reps)
+    del copies
     return {"us": ms * 1e3, "keys_per_s": n / (ms * 1e-3), "bytes": per,
             "GB_per_s": per / (ms * 1e6), "frac_hbm": per / (ms * 1e6) / HBM_PEAK_GBS,
             "copies": k}
@@ -570,6 +593,8 @@ def main():
                 r = {"us": ms * 1e3, "GB_per_s": sbytes / (ms * 1e6)}
         elif k == "write":
             r = time_write(torch, axr, stream, keys, bits, b, args.steps)
+        elif k == "fused":
+            r = time_fused(torch, axr, stream, keys, q, bits, b, args.steps)
         else:
             del keys
             if k == "qwen_score":
@@ -584,31 +609,44 @@ def main():
         print(json.dumps({"profile": k, **r}), flush=True)
         return
 
+    # A step quantizes every key (records and norms stored) and scores every
+    # query head against them: one launch of the quantize-and-score kernel.
+    # The same work as two launches (write kernel, then score kernel) is
+    # timed the same way beside it.
     def step():
+        axr.quantize_score(keys, q, bits, b, packed=packed, norms=norms, out=scores)
+
+    def step_two_launches():
         axr.quantize_keys(keys, bits, b, packed=packed, norms=norms)
         axr.score(q, packed, norms, bits, b, out=scores)
 
     # Steps run untimed for settle_ms first: a write + score loop starting
     # from an idle chip runs its first ~10 ms up to half slower while the
     # clock ramps; then the warmup steps, then the timed steps (wall clock
-    # between two synchronisations), then as many steps with HIP events
-    # around each kernel (on the stream the kernels run on) for the split.
+    # between two synchronisations), then as many two-launch steps with HIP
+    # events around each kernel (on the stream the kernels run on) for the
+    # split.
     log(f"settle {args.settle_ms:.0f} ms, warmup {args.warmup}, timing {args.steps} steps")
     gc.collect()
     gc.disable()
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < args.settle_ms * 1e-3:
-        for _ in range(16):
-            step()
+
+    def timed_steps(fn):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.settle_ms * 1e-3:
+            for _ in range(16):
+                fn()
+            torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            fn()
         torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    elapsed = timed_steps(step)
+    elapsed_two = timed_steps(step_two_launches)
     # The same number of steps again with HIP events around each kernel, for
     # the split between the two: an event recorded between the kernels costs
     # the GPU ~2 us, so these are not the timed steps.
@@ -622,6 +660,7 @@ def main():
     torch.cuda.synchronize()
     gc.enable()
     ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step_two = elapsed_two * 1e3 / args.steps
     step_write_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     step_score_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
 
@@ -632,6 +671,7 @@ def main():
         return graph_ms(torch, stream, fn, calls, reps)
 
     log("per-kernel timing")
+    fused_hbm = time_fused(torch, axr, stream, keys, q, bits, b, args.steps)
     write_hbm = time_write(torch, axr, stream, keys, bits, b, args.steps)
     score_hbm = time_score(torch, axr, stream, q, packed, norms, bits, b, args.steps)
     score_res_ms = per_graph_ms(lambda: axr.score(q, packed, norms, bits, b, out=scores),
@@ -779,6 +819,8 @@ def main():
                    "q_heads": Hq, "context": T, "d": d, "b": b, "key_dtype": "f16",
                    "query_dtype": "f16", "keys_per_step": n,
                    "arithmetic": "fp32 transform and norms, int32 fixed-point table sums",
+                   "step": "one axr_quantize_score launch: every key quantized (records "
+                           "and norms stored) and scored against every query head",
                    "settle_ms": args.settle_ms},
         "roofline": {"kernel": "score", "source": f"HBM ({score_hbm['copies']} rotating "
                                                   "copies of the cache)",
@@ -788,6 +830,20 @@ def main():
                      "traffic": counter_traffic("score"), "bytes_per_launch": sbytes,
                      "us": score_hbm["us"],
                      "valu_per_cu_cycle": valu_issue("score", score_hbm["us"])},
+        "roofline_fused": {"kernel": "quantize_score (the step)",
+                           "source": f"HBM ({fused_hbm['copies']} rotating copies of keys "
+                                     "and outputs)",
+                           "bound": "hbm", "achieved": round(fused_hbm["GB_per_s"], 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(fused_hbm["GB_per_s"] / HBM_PEAK_GBS, 4),
+                           "traffic": counter_traffic("fused"),
+                           "bytes_per_launch": fused_hbm["bytes"], "us": fused_hbm["us"],
+                           "valu_per_cu_cycle": valu_issue("fused", fused_hbm["us"])},
+        "step_two_launches": {"ms_per_step": ms_per_step_two,
+                              "value": n / (ms_per_step_two * 1e-3),
+                              "note": "the same step as the write kernel then the score "
+                                      "kernel, timed the same way right after the fused "
+                                      "steps"},
         "roofline_write": {"kernel": "write", "source": f"HBM ({write_hbm['copies']} rotating "
                                                         "copies of the keys)",
                            "bound": "hbm", "achieved": round(write_hbm["GB_per_s"], 1),

@@ -182,6 +182,30 @@ int axr_decode_step(const void* q, int q_dtype, const void* k_new, int k_dtype,
                     float* scores, void* stream);
 
 /*
+ * Write and read path in one launch (AXELRAM, Abstract: each key is
+ * transformed and quantized once on write; a query is scored by table lookup
+ * on the stored indices).  The effect of axr_quantize_keys over the n =
+ * B*Hkv*T keys of a dense cache followed by axr_score(t_cap = T): records,
+ * norms and scores are bit for bit those two calls' results.  Each block of
+ * the score kernel quantizes the keys of its tile with the write path's
+ * arithmetic, stores their records and norms, and scores them from
+ * registers, so the records are never read back.
+ *   keys   : device [B][Hkv][T][d] of k_dtype, 16-byte aligned
+ *   q      : device [B][Hq][d] of q_dtype, 16-byte aligned
+ *   packed : device uint32 [B][Hkv][T][W] (output), 16-byte aligned
+ *   norms  : device float [B][Hkv][T] (output), 4-byte aligned
+ *   scores : device float [B][Hq][T] (output), 4-byte aligned
+ * Built for d = 128, b = 2 or 3 and Hq / Hkv <= 4 (one table per (batch, KV
+ * head) row); other shapes return AXR_EUNSUPPORTED (use the two calls).
+ * Same further requirements as axr_score, plus T * d * sizeof(key) < 2^31.
+ * B = 0 or T = 0 is a no-op.  Errors: AXR_EINVAL, AXR_EUNSUPPORTED,
+ * AXR_EALIGN, AXR_EHIP.
+ */
+int axr_quantize_score(const void* keys, int k_dtype, const void* q, int q_dtype,
+                       const uint32_t* sign_bits, int B, int Hq, int Hkv, int64_t T, int d,
+                       int b, uint32_t* packed, float* norms, float* scores, void* stream);
+
+/*
  * Attention probabilities over the table-lookup scores, with the context split
  * across blocks.  The pages define the scores (AXELRAM, Abstract: score =
  * norm times the sum of table entries); the softmax over a row is the usual

@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "AxrError", "LIB_PATH", "lib", "version", "codebook", "sign_words",
-    "packed_words", "quantize_keys", "append_keys", "decode_step", "score", "score_softmax",
+    "packed_words", "quantize_keys", "append_keys", "decode_step", "quantize_score", "score",
+    "score_softmax",
     "score_softmax_noalloc",
     "transform", "sign_selection_errors", "sign_selection_choose", "select_sign_pattern",
     "quantize_keys_isoquant", "transform_isoquant",
@@ -92,6 +93,9 @@ def _load():
     so.axr_decode_step.restype = i32
     so.axr_decode_step.argtypes = [vp, i32, vp, i32, u32p, vp, i32, i32, i32, i64, i64, i32, i32,
                                    vp, vp, vp, vp]
+    so.axr_quantize_score.restype = i32
+    so.axr_quantize_score.argtypes = [vp, i32, vp, i32, u32p, i32, i32, i32, i64, i32, i32, vp,
+                                      vp, vp, vp]
     so.axr_transform.restype = i32
     so.axr_transform.argtypes = [vp, i32, i64, i32, u32p, i32, vp, vp]
     so.axr_probe_read_stream.restype = i32
@@ -239,6 +243,34 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, sign_bits, b: int, packed:
                                b, packed.data_ptr(), norms.data_ptr(), out.data_ptr(),
                                _stream(q)))
     return out
+
+
+def quantize_score(keys: torch.Tensor, q: torch.Tensor, sign_bits, b: int,
+                   packed: torch.Tensor = None, norms: torch.Tensor = None,
+                   out: torch.Tensor = None):
+    """Write and read path in one launch: keys [B, Hkv, T, d] and q [B, Hq, d]
+    -> (packed int32 [B, Hkv, T, W], norms fp32 [B, Hkv, T], scores fp32
+    [B, Hq, T]), the results of quantize_keys followed by score.  Built for
+    d = 128, b = 2 or 3 and Hq / Hkv <= 4."""
+    B, Hkv, T, d = keys.shape
+    Bq, Hq, dq = q.shape
+    if (Bq, dq) != (B, d):
+        raise ValueError("keys and q shapes disagree")
+    if packed is None:
+        packed = torch.empty(B, Hkv, T, packed_words(d, b), dtype=torch.int32, device=keys.device)
+    if norms is None:
+        norms = torch.empty(B, Hkv, T, dtype=torch.float32, device=keys.device)
+    if out is None:
+        out = torch.empty(B, Hq, T, dtype=torch.float32, device=keys.device)
+    _need_out(packed, (B, Hkv, T, packed_words(d, b)), torch.int32, "packed")
+    _need_out(norms, (B, Hkv, T), torch.float32, "norms")
+    _need_out(out, (B, Hq, T), torch.float32, "out")
+    _need_cuda(keys, q, packed, norms, out)
+    words, wp = _words_ptr(sign_words(sign_bits))
+    _check(lib.axr_quantize_score(keys.data_ptr(), _dtype_code(keys), q.data_ptr(),
+                                  _dtype_code(q), wp, B, Hq, Hkv, T, d, b, packed.data_ptr(),
+                                  norms.data_ptr(), out.data_ptr(), _stream(keys)))
+    return packed, norms, out
 
 
 def score(q: torch.Tensor, packed: torch.Tensor, norms: torch.Tensor, sign_bits, b: int,

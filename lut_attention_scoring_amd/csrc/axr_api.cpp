@@ -543,6 +543,42 @@ int axr_decode_step(const void* q, int q_dtype, const void* k_new, int k_dtype,
   return hip_status(err, "score kernel launch");
 }
 
+int axr_quantize_score(const void* keys, int k_dtype, const void* q, int q_dtype,
+                       const uint32_t* sign_bits, int B, int Hq, int Hkv, int64_t T, int d,
+                       int b, uint32_t* packed, float* norms, float* scores, void* stream) {
+  int rc = check_score_sizes(d, b, q_dtype, sign_bits, B, Hq, Hkv, T, T);
+  if (rc != AXR_OK) return rc;
+  if (!supported_dtype(k_dtype)) return fail(AXR_EUNSUPPORTED, "k_dtype=%d is not supported", k_dtype);
+  if (d != 128 || b > 3)
+    return fail(AXR_EUNSUPPORTED, "quantize-and-score is built for d=128 and b=2 or 3 (d=%d b=%d)",
+                d, b);
+  if (Hq / Hkv > 4)
+    return fail(AXR_EUNSUPPORTED, "quantize-and-score needs Hq/Hkv <= 4 (got %d)", Hq / Hkv);
+  // one row of raw keys is addressed with 32-bit offsets
+  const int64_t esize = k_dtype == AXR_F32 ? 4 : 2;
+  if (T > 0 && T * d * esize > INT32_MAX)
+    return fail(AXR_EUNSUPPORTED, "T=%lld tokens exceed 2 GiB of keys per row",
+                static_cast<long long>(T));
+  if (B == 0 || T == 0) return ok();
+  if (keys == nullptr || q == nullptr || packed == nullptr || norms == nullptr ||
+      scores == nullptr)
+    return fail(AXR_EINVAL, "keys, q, packed, norms and scores must be non-null");
+  if (!aligned(keys, 16) || !aligned(q, 16) || !aligned(packed, 16))
+    return fail(AXR_EALIGN, "keys, q and packed must be 16-byte aligned");
+  if (!aligned(norms, 4) || !aligned(scores, 4))
+    return fail(AXR_EALIGN, "norms and scores must be 4-byte aligned");
+  axr::ScoreParams p = score_params(sign_bits, Hq, Hkv, T, T, d, b, nullptr);
+  const axr::WriteParams wp = write_params(sign_bits, d, b);
+  for (int i = 0; i < axr::kMaxLevels / 2; ++i) p.tpos[i] = wp.tpos[i];
+  p.inv_sqrt_d = wp.inv_sqrt_d;
+  p.keys = keys;
+  p.kdt = k_dtype;
+  p.packed_out = packed;
+  p.norms_out = norms;
+  int err = axr::launch_score(q, q_dtype, packed, norms, B, d, b, p, scores, stream);
+  return hip_status(err, "quantize-and-score kernel launch");
+}
+
 int axr_score_ragged(const void* q, int q_dtype, const uint32_t* packed, const float* norms,
                      const uint32_t* sign_bits, int B, int Hq, int Hkv, const int32_t* lens,
                      int64_t T, int64_t t_cap, int d, int b, float* scores, void* stream) {

@@ -81,6 +81,12 @@ struct ScoreParams {
   uint32_t* packed_out;           // the cache (same buffers as packed / norms)
   float* norms_out;
   float tpos[kMaxLevels / 2];     // positive thresholds times sqrt(d)
+  // Optional quantize-and-score (keys != nullptr): the raw keys
+  // [B][Hkv][T][d] (dtype kdt) are quantized with the write path's rule, their
+  // records and norms stored in packed_out / norms_out (t_cap = T) and scored
+  // from registers.
+  const void* keys;
+  float inv_sqrt_d;               // 1 / sqrt(d), as the write path rounds it
 };
 
 // Library-held device scratch of axr_score_softmax_noalloc (split-T

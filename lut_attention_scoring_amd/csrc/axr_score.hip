@@ -47,6 +47,7 @@
 #include "axr.h"
 #include "axr_device.h"
 #include "axr_internal.h"
+#include "axr_keyquant.h"
 
 namespace axr {
 namespace {
@@ -276,10 +277,12 @@ __device__ __forceinline__ void buffer_load_words(uint32_t (&dst)[WL], __amdgpu_
 }
 
 // What a launch computes besides the scores: nothing, the split-T softmax
-// partials, or the fused decode step's new key.
-enum ScoreMode { kPlain = 0, kLse = 1, kDecode = 2 };
+// partials, the fused decode step's new key, or (kFused) the records and
+// norms of every key it scores, quantized from the raw keys (KDT their
+// dtype) in the same pass.
+enum ScoreMode { kPlain = 0, kLse = 1, kDecode = 2, kFused = 3 };
 
-template <int D, int BITS, int P, int NT, int NTHREADS, int MODE, bool SG>
+template <int D, int BITS, int P, int NT, int NTHREADS, int MODE, bool SG, int KDT = AXR_F16>
 __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict__ q, int qdt,
                                                        const uint32_t* __restrict__ packed,
                                                        const float* __restrict__ norms,
@@ -328,7 +331,16 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   // record units in flight per wave: the 4-coordinate table's units cost
   // the fewest instructions, so more of them are kept in flight (5 measured
   // fastest, against 3, 4, 6 and 8)
-  constexpr int PD = NT == 1 ? (P == 4 ? 5 : 3) : 2;
+  constexpr int PD = MODE == kFused ? (KDT == AXR_F32 ? 1 : 2)
+                                    : (NT == 1 ? (P == 4 ? 5 : 3) : 2);
+  // Fused quantize-and-score: a lane loads the raw words of its key's 32
+  // coordinates (the write path's layout at d = 128: lane u holds block u
+  // and quantizes it into exactly the b record words that it looks up).
+  constexpr bool FUSED = MODE == kFused;
+  static_assert(!FUSED || (S::LPK == 4 && NT == 1 && !SG && BITS <= 3),
+                "quantize-and-score is built for d = 128, b = 2 or 3, one head group");
+  constexpr int KW = FUSED ? RawWords<KDT>::kWords : 4;   // raw words per lane
+  constexpr uint32_t KEY_BYTES = D * (KDT == AXR_F32 ? 4u : 2u);
   // tokens [0, len) of this batch row are scored: T, or lens[bi] (clamped),
   // or pos[bi] + 1 in a fused decode step
   int64_t len = prm.T;
@@ -387,6 +399,24 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   if (tid == 0) next_unit = PD * NW;
   const uint32_t vrec = static_cast<uint32_t>(t0 + kw) * REC_BYTES + u * (S::WL * 4);
   const uint32_t vnrm = static_cast<uint32_t>(t0 + kw) * 4u;
+  // Fused: the raw keys of the row, through a resource that ends at the
+  // tile's last token (loads past it return zeros, a zero key, whose record
+  // is not stored), and the write path's per-lane sign pattern.
+  const __amdgpu_buffer_rsrc_t rkey = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(FUSED ? static_cast<const void*>(static_cast<const char*>(prm.keys) +
+                                                          rowbase * KEY_BYTES)
+                              : static_cast<const void*>(packed)),
+      0, static_cast<int>(FUSED ? static_cast<uint32_t>(t1) * KEY_BYTES : 0u), kRsrcWord3);
+  const uint32_t vkey = static_cast<uint32_t>(t0 + kw) * KEY_BYTES + u * (KEY_BYTES / S::LPK);
+  auto load_raw = [&](uint32_t (&r)[KW], uint32_t unit) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < KW / 4; ++i) {
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(
+          rkey, vkey + unit * (S::KPW * KEY_BYTES) + 16u * i, 0, 0);
+      r[4 * i] = v.x; r[4 * i + 1] = v.y; r[4 * i + 2] = v.z; r[4 * i + 3] = v.w;
+    }
+  };
 
   // 1. q' = H (s * q) / sqrt(d) for head g by wave g, in registers: lane l
   //    holds coordinates l + 64 r; butterflies over r in registers and over
@@ -420,13 +450,18 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   // build.
   uint32_t wq[PD][S::WL];
   float nq[PD];
+  uint32_t rq[FUSED ? PD : 1][KW];              // fused: raw key words in flight
   uint32_t ks[PD];                              // unit of each batch in flight
 #pragma unroll
   for (int pd = 0; pd < PD; ++pd) {
     ks[pd] = static_cast<uint32_t>(pd * NW) + wave_s;
-    buffer_load_words<S::WL>(wq[pd], rrec, vrec + ks[pd] * (S::KPW * REC_BYTES), 0);
-    nq[pd] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           rnrm, vnrm + ks[pd] * (S::KPW * 4u), 0, 0));
+    if constexpr (FUSED) {
+      load_raw(rq[pd], ks[pd]);
+    } else {
+      buffer_load_words<S::WL>(wq[pd], rrec, vrec + ks[pd] * (S::KPW * REC_BYTES), 0);
+      nq[pd] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rnrm, vnrm + ks[pd] * (S::KPW * 4u), 0, 0));
+    }
   }
 
   if (wave < GB) {
@@ -691,6 +726,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   for (int st = 0; st < S::NV; ++st) sgaddr[st] = boff[st];
   const uint32_t umask = (u & 1) ? 0x80808080u : 0u;
   const uint32_t c3f = 0x3Fu;
+  // Fused: the write path's sign pattern and lane-stage multipliers of the
+  // block this lane holds.
+  WhtLane<D, KDT> wht;
+  if constexpr (FUSED) wht.init(prm.sign, lane_block<S::LPK>(u));
   // Scores of this block's heads through a raw buffer resource (uniform
   // base: the block's first head row); each lane stores head u (and u + 4)
   // at a fixed per-lane offset plus a per-batch scalar offset.
@@ -754,10 +793,41 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
 #pragma unroll
       for (int il = 0; il < IL; ++il) {
         const int pd = pd0 + il;
+        kc[il] = ks[pd];
+        if constexpr (FUSED) {
+          // quantize the unit's keys exactly as the write kernel does, store
+          // their records and norms, and score them from registers
+          uint32_t raw[KW];
+#pragma unroll
+          for (int i = 0; i < KW; ++i) raw[i] = rq[pd][i];
+          ks[pd] = kn + il;
+          load_raw(rq[pd], ks[pd]);
+          float x[32];
+          float nr = wht.transform(raw, x);
+          nr = rescued_key_norm<S::LPK>(nr, x, prm.inv_sqrt_d);
+          float th[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) th[i] = prm.tpos[i] * nr;
+          quantize_lane<BITS>(x, th, w[il]);
+          nk[il] = nr;
+          const uint32_t tb_rel = kc[il] * S::KPW;
+          if (tb_rel + kw < tile_keys) {
+            const size_t rowk = rowbase + static_cast<size_t>(t0) + tb_rel + kw;
+            uint32_t* dst = prm.packed_out + rowk * S::W + u * BITS;
+            if constexpr (BITS == 2) {
+              *reinterpret_cast<uint2*>(dst) = make_uint2(w[il][0], w[il][1]);
+            } else {
+#pragma unroll
+              for (int i = 0; i < BITS; ++i) dst[i] = w[il][i];
+            }
+            if (u == 0) prm.norms_out[rowk] = nr;
+          }
+          rotate_right<S::WL>(w[il], rot);
+          continue;
+        }
 #pragma unroll
         for (int i = 0; i < S::WL; ++i) w[il][i] = wq[pd][i];
         nk[il] = nq[pd];
-        kc[il] = ks[pd];
         if (MODE == kDecode && holds_new) {
           // the new token's record comes from LDS, not from the cache
           if (t0 + static_cast<int64_t>(kc[il]) * S::KPW + kw == slot) {
@@ -967,7 +1037,8 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
   p.heads_per_block = 4 * NT;
   p.head_groups = (p.G + 4 * NT - 1) / (4 * NT);
   const int64_t rows = static_cast<int64_t>(B) * p.Hkv * p.head_groups;   // block rows
-  const int mode = p.knew != nullptr ? kDecode : (p.partials != nullptr ? kLse : kPlain);
+  const int mode = p.keys != nullptr ? kFused
+                  : (p.knew != nullptr ? kDecode : (p.partials != nullptr ? kLse : kPlain));
   // One block per CU, each with one tile: a second resident block would
   // halve the tile over which the table build is spread, and the loop is
   // issue-bound either way.
@@ -990,7 +1061,26 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
     return 0;
   }
   const dim3 g(static_cast<unsigned>(grid)), blk(NTHREADS);
-  if (mode == kDecode) {
+  if (mode == kFused) {
+    if constexpr (S::LPK == 4 && NT == 1 && !SG && BITS <= 3) {
+      switch (p.kdt) {
+        case AXR_F32:
+          hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kFused, SG, AXR_F32>), g,
+                             blk, 0, s, q, qdt, packed, norms, scores, p);
+          break;
+        case AXR_F16:
+          hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kFused, SG, AXR_F16>), g,
+                             blk, 0, s, q, qdt, packed, norms, scores, p);
+          break;
+        default:
+          hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kFused, SG, AXR_BF16>), g,
+                             blk, 0, s, q, qdt, packed, norms, scores, p);
+          break;
+      }
+    } else {
+      return static_cast<int>(hipErrorInvalidValue);   // the C ABI rejects these shapes
+    }
+  } else if (mode == kDecode) {
     hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kDecode, SG>), g, blk, 0, s, q,
                        qdt, packed, norms, scores, p);
   } else if (mode == kLse) {

@@ -120,6 +120,34 @@ def test_score_validation():
     assert _s(B=0, q=None, packed=None, norms=None, scores=None)[0] == axr.OK
 
 
+def _qs(keys=FAKE, kdt=axr.F16, q=FAKE, qdt=axr.F16, signs=SIGNS, B=2, Hq=8, Hkv=2, T=64,
+        d=128, b=3, packed=FAKE, norms=FAKE, scores=FAKE):
+    return _status(axr.lib.axr_quantize_score, keys, kdt, q, qdt, signs, B, Hq, Hkv, T, d, b,
+                   packed, norms, scores, None)
+
+
+def test_quantize_score_validation():
+    # shapes the one-launch path is not built for are rejected, not routed
+    assert _qs(d=256)[0] == axr.EUNSUPPORTED
+    assert _qs(b=4)[0] == axr.EUNSUPPORTED
+    assert _qs(Hq=16, Hkv=2)[0] == axr.EUNSUPPORTED
+    assert _qs(kdt=7)[0] == axr.EUNSUPPORTED
+    assert _qs(qdt=7)[0] == axr.EUNSUPPORTED
+    assert _qs(T=(1 << 23) + 1)[0] == axr.EUNSUPPORTED     # > 2 GiB of fp16 keys per row
+    assert _qs(Hq=6, Hkv=4)[0] == axr.EINVAL
+    assert _qs(B=-1)[0] == axr.EINVAL
+    assert _qs(keys=None)[0] == axr.EINVAL
+    assert _qs(scores=None)[0] == axr.EINVAL
+    assert _qs(signs=None)[0] == axr.EINVAL
+    assert _qs(keys=FAKE + 8)[0] == axr.EALIGN
+    assert _qs(packed=FAKE + 4)[0] == axr.EALIGN
+    assert _qs(norms=FAKE + 2)[0] == axr.EALIGN
+    st, msg = _qs(b=4)
+    assert "b=4" in msg
+    assert _qs(T=0, keys=None, q=None, packed=None, norms=None, scores=None)[0] == axr.OK
+    assert _qs(B=0, keys=None, q=None, packed=None, norms=None, scores=None)[0] == axr.OK
+
+
 def test_transform_validation():
     f = axr.lib.axr_transform
     assert _status(f, FAKE, axr.F32, 4, 48, SIGNS, 1, FAKE, None)[0] == axr.EUNSUPPORTED

@@ -1,0 +1,131 @@
+"""GPU parity of the one-launch write and read path, axr_quantize_score
+("AXELRAM: Quantize Once, Never Dequantize", Abstract: a key is transformed
+and quantized once, on write, and scored by table lookup on its stored
+indices).  Its records, norms and scores must equal, bit for bit, those of
+axr_quantize_keys followed by axr_score on the same inputs; on smaller shapes
+they are also checked against the oracle (indices by the boundary rule,
+norms, and scores given the GPU's own indices)."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import axelram as A
+from tests._parity import f64, words_u32, assert_indices, assert_scores, assert_norms
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import lut_attention_scoring_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+
+
+def axr():
+    import lut_attention_scoring_amd as m
+    return m
+
+
+def _inputs(rng, B, Hkv, Hq, T, dtype, scale=2.0):
+    keys = torch.from_numpy((rng.standard_normal((B, Hkv, T, 128)) * scale).astype(np.float32))
+    q = torch.from_numpy(rng.standard_normal((B, Hq, 128)).astype(np.float32))
+    return keys.to(dtype), q.to(dtype)
+
+
+def _same(keys, q, bits, b, label):
+    """Fused launch against the two launches, bit for bit; returns the
+    fused outputs (on the CPU)."""
+    m = axr()
+    kd, qd = keys.to(DEV), q.to(DEV)
+    p2, n2 = m.quantize_keys(kd, bits, b)
+    s2 = m.score(qd, p2, n2, bits, b)
+    # outputs pre-filled with junk: every element must be written
+    B, Hkv, T, _ = keys.shape
+    pf = torch.full((B, Hkv, T, 128 * b // 32), -7, dtype=torch.int32, device=DEV)
+    nf = torch.full((B, Hkv, T), float("nan"), device=DEV)
+    sf = torch.full((B, q.shape[1], T), float("nan"), device=DEV)
+    m.quantize_score(kd, qd, bits, b, packed=pf, norms=nf, out=sf)
+    torch.cuda.synchronize()
+    assert torch.equal(pf, p2), f"{label}: records differ"
+    assert torch.equal(nf.view(torch.int32), n2.view(torch.int32)), f"{label}: norms differ"
+    assert torch.equal(sf.view(torch.int32), s2.view(torch.int32)), f"{label}: scores differ"
+    return pf.cpu(), nf.cpu(), sf.cpu()
+
+
+SHAPES = [  # (B, Hkv, Hq, T)
+    (2, 3, 12, 1000),    # G = 4, ragged tail
+    (1, 2, 2, 17),       # G = 1, one full unit and one key
+    (3, 1, 3, 5000),     # G = 3 (a padded head slot)
+    (1, 4, 8, 16),       # G = 2, exactly one unit
+    (1, 1, 1, 4096),     # the tiny workload's shape
+    (2, 2, 8, 40000),    # several tiles per row
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("b", [2, 3])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_fused_matches_two_launches(shape, b, dtype):
+    B, Hkv, Hq, T = shape
+    rng = np.random.default_rng(7000 + 97 * T + 13 * Hq + b)
+    keys, q = _inputs(rng, B, Hkv, Hq, T, dtype)
+    print(f"fused vs two launches {shape} b={b} {dtype}", flush=True)
+    _same(keys, q, W.sign_bits(128), b, f"{shape} b={b} {dtype}")
+
+
+@pytest.mark.parametrize("b", [2, 3])
+def test_fused_against_oracle(b):
+    B, Hkv, Hq, T = 2, 2, 8, 700
+    rng = np.random.default_rng(7100 + b)
+    keys, q = _inputs(rng, B, Hkv, Hq, T, torch.float16)
+    bits = W.sign_bits(128)
+    pf, nf, sf = _same(keys, q, bits, b, f"oracle b={b}")
+    s = A.signs_from_bits(bits)
+    c, t = A.lloyd_max_codebook(128, b)
+    y, onorm = A.transform_keys(f64(keys), s)
+    oidx = A.quantize(y, t)
+    gidx = A.unpack_indices(words_u32(pf), 128, b)
+    assert_indices(gidx, oidx, y, t, f"fused b={b}")
+    assert_norms(f64(nf), onorm, f"fused b={b}")
+    qp = A.transform_queries(f64(q), s)
+    assert_scores(f64(sf), qp, gidx, onorm, c, f"fused b={b}")
+
+
+@pytest.mark.parametrize("scale", [1e-25, 1e30])
+def test_fused_extreme_magnitudes(scale):
+    """Keys whose squares underflow or overflow fp32 (the norm is taken again
+    from the scaled transformed coordinates), mixed with ordinary keys in the
+    same waves."""
+    rng = np.random.default_rng(7200)
+    keys, q = _inputs(rng, 1, 2, 8, 300, torch.float32)
+    keys[:, :, ::3] *= scale
+    _same(keys, q, W.sign_bits(128), 3, f"extreme {scale}")
+
+
+def test_fused_llama_full_size():
+    """The LLaMA-shaped decode cache at full size (2,097,152 keys, the
+    benchmark's step): bit for bit the two launches."""
+    w = W.llama_decode()
+    print("fused vs two launches, LLaMA decode cache", flush=True)
+    _same(w["keys"], w["q"], w["sign_bits"], w["b"], "llama full size")
+
+
+def test_fused_tiny_workload_oracle():
+    """The tiny workload (fp32 keys, one head) in one launch against the oracle."""
+    w = W.tiny()
+    bits, b = w["sign_bits"], w["b"]
+    pf, nf, sf = _same(w["keys"], w["q"], bits, b, "tiny")
+    s = A.signs_from_bits(bits)
+    c, t = A.lloyd_max_codebook(128, b)
+    y, onorm = A.transform_keys(f64(w["keys"]), s)
+    oidx = A.quantize(y, t)
+    gidx = A.unpack_indices(words_u32(pf), 128, b)
+    assert_indices(gidx, oidx, y, t, "tiny fused")
+    assert_norms(f64(nf), onorm, "tiny fused")
+    assert_scores(f64(sf), A.transform_queries(f64(w["q"]), s), gidx, onorm, c, "tiny fused")
