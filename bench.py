@@ -275,6 +275,19 @@ def time_write(torch, axr, stream, keys, bits, b, reps):
             "copies": k}
 
 
+def table_read_bytes_per_key(d, b, G):
+    """LDS bytes of table entries the score kernel reads per key: d/P lookups
+    of 16 bytes (four heads) per group of four query heads, with P the
+    coordinates per table entry that the library picks for (d, b)."""
+    if d == 128:
+        p = 4 if b == 2 else 2
+    elif b == 4 or (d == 512 and b == 3):
+        p = 1
+    else:
+        p = 2
+    return (d // p) * ((G + 3) // 4) * 16
+
+
 def time_fused(torch, axr, stream, keys, q, bits, b, reps):
     """Quantize-and-score over rotating copies of the keys, each with its own
     records, norms and score rows."""
@@ -311,8 +324,11 @@ def time_score(torch, axr, stream, q, packed, norms, bits, b, reps, min_copies=4
     rot = Rotor(copies, lambda c: axr.score(q, c[0], c[1], bits, b, out=c[2]))
     ms = graph_ms(torch, stream, rot, graph_calls(k), reps)
     del copies
+    lds = n * table_read_bytes_per_key(d, b, Hq // Hkv)
     return {"us": ms * 1e3, "keys_per_s": n / (ms * 1e-3),
             "head_scores_per_s": n * (Hq // Hkv) / (ms * 1e-3), "bytes": per,
+            "lds_table_bytes": lds,
+            "lds_B_per_cu_cycle": round(lds / (CUS * CLOCK_HZ * ms * 1e-3), 1),
             "GB_per_s": per / (ms * 1e6), "frac_hbm": per / (ms * 1e6) / HBM_PEAK_GBS,
             "copies": k}
 
@@ -381,6 +397,8 @@ def configs_section(torch, axr, W, stream, reps):
         "write_frac_hbm": wb * L / (wms * 1e6) / HBM_PEAK_GBS,
         "score_frac_hbm": sb * L / (sms * 1e6) / HBM_PEAK_GBS,
         "score_keys_per_s": n * L / (sms * 1e-3), "write_keys_per_s": n * L / (wms * 1e-3),
+        "score_lds_B_per_cu_cycle": round(n * L * table_read_bytes_per_key(d, 4, Hq // Hkv) /
+                                          (CUS * CLOCK_HZ * sms * 1e-3), 1),
         "note": "one pass = every layer back to back on its own cache (layer sum); "
                 f"{passes} passes timed"}
     del lk, lq, lp, ls
@@ -753,6 +771,14 @@ def main():
         Rotor(regions, lambda c: axr.probe_read_write(c[0], score_in, c[1], score_out)),
         args.steps, graph_calls(len(regions)))
     del regions, kb
+    # LDS: the score kernel's table-read pattern in a bare loop, one
+    # 1024-thread block per CU (include/axr_probe.h)
+    lds_out = torch.empty(262144, dtype=torch.int32, device=dev)
+    lds_iters = 256
+    lds_bytes_cu = axr.probe_lds_read(lds_iters, lds_out)
+    lds_ms = per_launch_ms(lambda: axr.probe_lds_read(lds_iters, lds_out), 20)
+    lds_peak = lds_bytes_cu / (lds_ms * 1e-3 * CLOCK_HZ)
+    del lds_out
     write_in = n * d * keys.element_size()
     write_out = n * (d * b // 8 + 4)
     wscratch = torch.empty(write_out, dtype=torch.uint8, device=dev)
@@ -829,7 +855,15 @@ def main():
                      "frac": round(score_hbm["GB_per_s"] / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic("score"), "bytes_per_launch": sbytes,
                      "us": score_hbm["us"],
-                     "valu_per_cu_cycle": valu_issue("score", score_hbm["us"])},
+                     "valu_per_cu_cycle": valu_issue("score", score_hbm["us"]),
+                     "lds": {"table_bytes_per_launch": score_hbm["lds_table_bytes"],
+                             "achieved_B_per_cu_cycle": score_hbm["lds_B_per_cu_cycle"],
+                             "probe_B_per_cu_cycle": round(lds_peak, 1),
+                             "frac": round(score_hbm["lds_B_per_cu_cycle"] / lds_peak, 3),
+                             "note": "16-byte table reads per launch (d/P lookups per key "
+                                     "per group of four heads) against a bare loop of the "
+                                     "same reads (include/axr_probe.h), per CU-cycle at "
+                                     "2.4 GHz"}},
         "roofline_fused": {"kernel": "quantize_score (the step)",
                            "source": f"HBM ({fused_hbm['copies']} rotating copies of keys "
                                      "and outputs)",
@@ -868,6 +902,8 @@ def main():
             "write_shaped_stream_us": wshaped_ms * 1e3,
             "write_shaped_stream_GB_per_s": wbytes / (wshaped_ms * 1e6),
             "write_frac_of_shaped_stream": wshaped_ms / (write_hbm["us"] * 1e-3),
+            "lds_read_B_per_cu_cycle": lds_peak,
+            "lds_read_probe_us": lds_ms * 1e3,
         },
         "kernels": {
             "write_hbm": write_hbm,

@@ -26,6 +26,7 @@ __all__ = [
     "quantize_keys_isoquant", "transform_isoquant",
     "probe_read_stream",
     "probe_read_write",
+    "probe_lds_read",
     "F32", "F16", "BF16",
 ]
 
@@ -102,6 +103,8 @@ def _load():
     so.axr_probe_read_stream.argtypes = [vp, i64, vp, vp]
     so.axr_probe_read_write.restype = i32
     so.axr_probe_read_write.argtypes = [vp, i64, vp, i64, vp]
+    so.axr_probe_lds_read.restype = i32
+    so.axr_probe_lds_read.argtypes = [i32, vp, vp]
     return so
 
 
@@ -511,3 +514,16 @@ def probe_read_write(src: torch.Tensor, in_bytes: int, dst: torch.Tensor, out_by
     if lib.axr_probe_read_write(src.data_ptr(), int(in_bytes), dst.data_ptr(), int(out_bytes),
                                 _stream(src)) != 0:
         raise AxrError(EINVAL, "axr_probe_read_write rejected its arguments")
+
+
+def probe_lds_read(iters: int, out: torch.Tensor):
+    """LDS probe (include/axr_probe.h): 256 blocks x 1024 threads read their
+    128 KiB LDS array with 16-byte reads in the score kernel's table pattern,
+    iters x 16 reads per thread; out is an int32 device tensor of >= 262144
+    elements (checksums).  Returns the bytes read per CU."""
+    if out.numel() * out.element_size() < 4 * 262144:
+        raise ValueError("out must hold 262144 uint32 checksums")
+    _need_cuda(out)
+    if lib.axr_probe_lds_read(int(iters), out.data_ptr(), _stream(out)) != 0:
+        raise AxrError(EINVAL, "axr_probe_lds_read rejected its arguments")
+    return 1024 * 16 * int(iters) * 16

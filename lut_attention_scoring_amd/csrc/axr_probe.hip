@@ -46,7 +46,53 @@ __global__ __launch_bounds__(kThreads) void read_write_stream(const uint4* __res
   for (int64_t o = o0 + threadIdx.x; o < o1; o += kThreads) out[o] = acc + static_cast<uint32_t>(o);
 }
 
+// LDS table-read loop: every thread owns 16 addresses in the score kernel's
+// pattern (row from a per-lane xorshift hash, column (step + key slot + 4u)
+// mod 16 for lane u of a 4-lane key); each pass xors a uniform value into the
+// row bits, which keeps the columns and moves the rows.  Every address is
+// masked to the 128 KiB array.
+constexpr int kLdsEntries = 8192;   // 16-byte entries
+__global__ __launch_bounds__(1024) void lds_read(int iters, uint32_t* __restrict__ out) {
+  __shared__ uint4 tab[kLdsEntries];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kLdsEntries; i += 1024)
+    tab[i] = make_uint4(i, i * 3u, i * 5u, i * 7u);
+  __syncthreads();
+  const uint32_t lane = tid % 64, u = lane % 4, kslot = (lane / 4) % 4;
+  uint32_t h = 0x9E3779B9u ^ (static_cast<uint32_t>(tid + 1024 * blockIdx.x) * 0x85EBCA6Bu);
+  uint32_t addr[16];
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    h ^= h << 13;
+    h ^= h >> 17;
+    h ^= h << 5;
+    addr[st] = u * 32768u + ((h >> 9) & 127u) * 256u + 16u * ((st + kslot + 4u * u) & 15u);
+  }
+  uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+  const char* base = reinterpret_cast<const char*>(tab);
+  for (int it = 0; it < iters; ++it) {
+    const uint32_t r = ((static_cast<uint32_t>(it) * 0x35u) & 127u) << 8;
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const uint4 e = *reinterpret_cast<const uint4*>(base + ((addr[st] ^ r) & (kLdsEntries * 16u - 16u)));
+      a0 += e.x;
+      a1 += e.y;
+      a2 += e.z;
+      a3 += e.w;
+    }
+  }
+  out[blockIdx.x * 1024 + tid] = a0 ^ a1 ^ a2 ^ a3;
+}
+
 }  // namespace
+
+extern "C" int axr_probe_lds_read(int iters, uint32_t* out, void* stream) {
+  if (out == nullptr || iters < 1 || iters > 65536 || (reinterpret_cast<uintptr_t>(out) & 3) != 0)
+    return -1;
+  hipLaunchKernelGGL(lds_read, dim3(256), dim3(1024), 0, static_cast<hipStream_t>(stream), iters,
+                     out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
 
 extern "C" int axr_probe_read_stream(const void* buf, int64_t bytes, uint32_t* sink,
                                      void* stream) {
