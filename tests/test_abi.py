@@ -148,6 +148,17 @@ def test_quantize_score_validation():
     assert _qs(B=0, keys=None, q=None, packed=None, norms=None, scores=None)[0] == axr.OK
 
 
+def test_probe_validation():
+    # the measurement probes reject bad arguments before any HIP call
+    f = axr.lib.axr_probe_lds_read
+    assert f(0, FAKE, None) == -1
+    assert f(65537, FAKE, None) == -1
+    assert f(4, None, None) == -1
+    assert f(4, FAKE + 2, None) == -1
+    assert axr.lib.axr_probe_read_stream(FAKE, 24, FAKE, None) == -1        # not a multiple of 16
+    assert axr.lib.axr_probe_read_write(FAKE, 16, FAKE + 1, 4, None) == -1  # misaligned output
+
+
 def test_transform_validation():
     f = axr.lib.axr_transform
     assert _status(f, FAKE, axr.F32, 4, 48, SIGNS, 1, FAKE, None)[0] == axr.EUNSUPPORTED
