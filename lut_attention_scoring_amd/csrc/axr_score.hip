@@ -31,6 +31,11 @@
 //     that the SIMD's issue arbitration favours take more units and all
 //     waves of the block finish together.  The blocks of a row's head
 //     groups, which read the same records, run on one XCD.
+//   * quantize-and-score (mode kFused, d = 128, b = 2 or 3, one head group):
+//     each wave loads the raw keys of its unit instead of records, quantizes
+//     them with the write path's lane arithmetic (lane u holds block u,
+//     whose b record words it then looks up), stores records and norms, and
+//     scores them from registers, so the records are never read back.
 //   * LDS banks: 16-byte reads are conflict-free when the 16 lanes of a
 //     quarter-wave touch 16 different 16-byte columns of a 256-byte row.  The
 //     table puts group v of lane-chunk u in column (v + KPG*u) mod 16 and each
@@ -758,9 +763,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
     ginv2_u[t4] = hinv2[(4 * t4 + u) % GB];
   }
 
-  // 3. stream the tile, keeping PD units of records in flight and working
-  //    on IL of them at once (independent lookups interleave in the LDS
-  //    queue).  A unit past the tile end is computed but not stored.
+  // 3. stream the tile, keeping PD units of records (fused: raw keys) in
+  //    flight and working on IL of them at once (independent lookups
+  //    interleave in the LDS queue).  A unit past the tile end is computed
+  //    but not stored.
   // softmax partials of the heads this lane stores: with four lanes per key
   // heads 4 * k + u (k < NT), otherwise head u
   constexpr int NSLOT = S::LPK == 4 ? NT : 1;
