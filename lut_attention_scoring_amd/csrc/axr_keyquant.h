@@ -1,6 +1,6 @@
 // Per-lane write-path arithmetic shared by the kernels that quantize keys:
-// the write kernel, and the score kernel when it appends the new key of a
-// decode step.  A key of d coordinates is held by LPK = d/32 adjacent lanes
+// the write kernel, and the score kernel when it quantizes the keys it
+// scores (quantize-and-score).  A key of d coordinates is held by LPK = d/32 adjacent lanes
 // of a wave (lane u owns the 32 coordinates of block lane_block(u), see
 // below); every lane of the wave must be active, since the transform
 // exchanges values across lanes.
@@ -203,40 +203,70 @@ __device__ __forceinline__ float rescued_key_norm(float nrm, const float (&x)[32
 
 // The sign pattern and the Walsh-Hadamard transform for one lane of a key,
 // the lane holding coordinate block blk = lane_block(u).  transform() leaves
-// z = H (s * k) (no 1/sqrt(d)) in x and returns ||k||.
+// z = H (s * k) (no 1/sqrt(d)) in x and returns ||k||.  The per-word sign
+// masks depend only on the block: kernels keep them in LDS (fill_sign_masks,
+// one row of NW words per block, read back with 16-byte broadcast loads by
+// transform_lds) rather than in NW registers per lane.
 template <int D, int DT>
 struct WhtLane {
   static constexpr int LPK = D / 32;
   static constexpr int NW = RawWords<DT>::kWords;
   static constexpr bool kDotStage = DT != AXR_F32 && LPK >= 8;
-  // fp16 / bf16: per raw word, the pair (+-1, +-1) in the key's format that
-  // multiplies its two coordinates (only its sign bits without the dot
-  // product stage); fp32: the sign bit to xor into each coordinate
-  uint32_t sg[NW];
   float m1, m2, m7, m8;
 
-  // The sign pattern of the block's 32 coordinates, times -1 throughout
-  // when popcount(blk) is odd (which makes every lane stage a single fused
-  // multiply-add), and the lane-stage multipliers from the bits of blk.
-  __device__ __forceinline__ void init(const uint32_t* sign_words, int blk) {
-    const uint32_t sw = sign_words[blk] ^ ((__popc(blk) & 1) ? 0xFFFFFFFFu : 0u);
+  // Word i of the block's sign masks, from its sign word sw (the sign
+  // pattern of the block's 32 coordinates, times -1 throughout when
+  // popcount(blk) is odd, which makes every lane stage a single fused
+  // multiply-add): for fp16 / bf16 the pair (+-1, +-1) in the key's format
+  // that multiplies the word's two coordinates (only its sign bits without
+  // the dot product stage); for fp32 the sign bit to xor into coordinate i.
+  static __device__ __forceinline__ uint32_t sign_mask(uint32_t sw, int i) {
     constexpr uint32_t one = DT == AXR_F16 ? 0x3C00u : 0x3F80u;   // 1.0 in the half format
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      if constexpr (DT == AXR_F32) {
-        sg[i] = ((sw >> i) & 1u) << 31;
-      } else {
-        sg[i] = ((((sw >> (2 * i)) & 1u) << 15) | (((sw >> (2 * i + 1)) & 1u) << 31)) |
-                (kDotStage ? one * 0x10001u : 0u);
-      }
+    if constexpr (DT == AXR_F32) {
+      return ((sw >> i) & 1u) << 31;
+    } else {
+      return ((((sw >> (2 * i)) & 1u) << 15) | (((sw >> (2 * i + 1)) & 1u) << 31)) |
+             (kDotStage ? one * 0x10001u : 0u);
     }
+  }
+
+  static __device__ __forceinline__ uint32_t sign_word(const uint32_t* sign_words, int blk) {
+    return sign_words[blk] ^ ((__popc(blk) & 1) ? 0xFFFFFFFFu : 0u);
+  }
+
+  // All LPK rows of sign masks into lds[LPK * NW] (block b's row at b * NW),
+  // by the calling block's threads; the caller synchronises before use.
+  static __device__ __forceinline__ void fill_sign_masks(uint32_t* lds, const uint32_t* sign_words,
+                                                         int tid, int nthreads) {
+    for (int t = tid; t < LPK * NW; t += nthreads) lds[t] = sign_mask(sign_word(sign_words, t / NW), t % NW);
+  }
+
+  // The lane-stage multipliers from the bits of blk.
+  __device__ __forceinline__ void init(int blk) {
     m1 = (blk & 1) ? 1.0f : -1.0f;
     m2 = (blk & 2) ? 1.0f : -1.0f;
     m7 = (blk & 4) ? 1.0f : -1.0f;
     m8 = (blk & 8) ? 1.0f : -1.0f;
   }
 
-  __device__ __forceinline__ float transform(const uint32_t (&raw)[NW], float (&x)[32]) const {
+  // The transform with the block's sign masks read from its LDS row
+  // (16-byte aligned).
+  __device__ __forceinline__ float transform_lds(const uint32_t (&raw)[NW], float (&x)[32],
+                                                 const uint4* row) const {
+    uint32_t sg[NW];
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+      const uint4 v = row[i];
+      sg[4 * i] = v.x;
+      sg[4 * i + 1] = v.y;
+      sg[4 * i + 2] = v.z;
+      sg[4 * i + 3] = v.w;
+    }
+    return transform(raw, x, sg);
+  }
+
+  __device__ __forceinline__ float transform(const uint32_t (&raw)[NW], float (&x)[32],
+                                             const uint32_t (&sg)[NW]) const {
     // Sum of squares (sign-independent), and the first butterfly stage
     // fused with the sign pattern and the conversion to fp32.  For the
     // half formats with d >= 256 that stage is a dot product of the raw

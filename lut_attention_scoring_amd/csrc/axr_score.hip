@@ -580,6 +580,14 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
     }
     if (lane == 0) newnrm = nrm;
   }
+  // Fused: the write path's sign masks of the key's four blocks, one LDS row
+  // per block (by the waves that hold no query head)
+  __shared__ uint4 sgl[FUSED ? S::LPK * KW / 4 : 1];
+  if constexpr (FUSED) {
+    if (tid >= 64 * GB)
+      WhtLane<D, KDT>::fill_sign_masks(reinterpret_cast<uint32_t*>(sgl), prm.sign, tid - 64 * GB,
+                                       NTHREADS - 64 * GB);
+  }
   __syncthreads();
 
   // ... and packs them into the record: thread i of the last wave assembles
@@ -735,7 +743,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   // Fused: the write path's sign pattern and lane-stage multipliers of the
   // block this lane holds.
   WhtLane<D, KDT> wht;
-  if constexpr (FUSED) wht.init(prm.sign, lane_block<S::LPK>(u));
+  if constexpr (FUSED) wht.init(lane_block<S::LPK>(u));
   // Scores of this block's heads through a raw buffer resource (uniform
   // base: the block's first head row); each lane stores head u (and u + 4)
   // at a fixed per-lane offset plus a per-batch scalar offset.
@@ -810,7 +818,11 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
           ks[pd] = kn + il;
           load_raw(rq[pd], ks[pd]);
           float x[32];
-          float nr = wht.transform(raw, x);
+          // the row offset through an empty asm keeps the mask reads in the
+          // loop (hoisted, they would hold KW registers throughout)
+          uint32_t srow = static_cast<uint32_t>(lane_block<S::LPK>(u)) * (KW / 4);
+          asm volatile("" : "+v"(srow));
+          float nr = wht.transform_lds(raw, x, &sgl[srow]);
           nr = rescued_key_norm<S::LPK>(nr, x, prm.inv_sqrt_d);
           float th[8];
 #pragma unroll

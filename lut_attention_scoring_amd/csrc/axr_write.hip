@@ -99,7 +99,11 @@ void write_kernel(const void* __restrict__ keys, int64_t n, WriteParams prm,
   // the block of the key this lane loads, transforms and stores
   const int blk = TF == kWht ? lane_block<LPK>(u) : u;
   WhtLane<D, DT> wht;
-  if constexpr (TF == kWht) wht.init(prm.sign, blk);
+  if constexpr (TF == kWht) wht.init(blk);
+  // the sign masks of every block of a key, one LDS row per block
+  __shared__ uint4 sgl[TF == kWht ? LPK * NW / 4 : 1];
+  if constexpr (TF == kWht)
+    WhtLane<D, DT>::fill_sign_masks(reinterpret_cast<uint32_t*>(sgl), prm.sign, threadIdx.x, kBlock);
   float P[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) P[i] = prm.tpos[i];
@@ -110,8 +114,8 @@ void write_kernel(const void* __restrict__ keys, int64_t n, WriteParams prm,
   if constexpr (BITS == 4) {
     for (int c = threadIdx.x; c < kCells; c += kBlock)
       cells[c] = make_uint2(prm.cells[2 * c], prm.cells[2 * c + 1]);
-    __syncthreads();
   }
+  if constexpr (BITS == 4 || TF == kWht) __syncthreads();
   // quaternions of this lane's eight blocks (comparison transform only)
   float qa[8][4], qb[8][4];
   if constexpr (TF != kWht) {
@@ -150,7 +154,11 @@ void write_kernel(const void* __restrict__ keys, int64_t n, WriteParams prm,
     float x[32];
     float nrm;
     if constexpr (TF == kWht) {
-      nrm = wht.transform(raw, x);
+      // the row offset through an empty asm: the reads stay in the loop
+      // (hoisted, the masks would hold NW registers for the whole kernel)
+      uint32_t srow = static_cast<uint32_t>(blk) * (NW / 4);
+      asm volatile("" : "+v"(srow));
+      nrm = wht.transform_lds(raw, x, &sgl[srow]);
     } else {
       // comparison transform: plain conversion, then the block rotations
       float ss = 0.0f;
