@@ -72,11 +72,11 @@ __device__ __forceinline__ void quat_block(float* v, const float (&a)[4], const 
   }
 }
 
-// Waves per SIMD the compiler is asked to fit: 6 (at most 80 VGPRs) for the
-// fp16 d = 128 Hadamard kernels with 2 or 3 bits, which would otherwise take
-// 81-82 VGPRs and run 5 waves per SIMD; the other instances already fit 6
-// waves or would spill under the cap, and keep the compiler's choice (1 sets
-// no bound).
+// Waves per SIMD the compiler is asked to fit at least: 6 (at most 80 VGPRs)
+// for the fp16 d = 128 Hadamard kernels with 2 or 3 bits, which once took
+// 81-82 VGPRs and ran 5 waves per SIMD (with the sign masks in LDS they take
+// ~62 and fit 8 by themselves); the other instances keep the compiler's
+// choice (1 sets no bound).
 template <int D, int BITS, int DT, int TF>
 constexpr int write_waves() {
   return (D == 128 && BITS <= 3 && DT == AXR_F16 && TF == kWht) ? 6 : 1;
