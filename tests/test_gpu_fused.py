@@ -110,10 +110,27 @@ def test_fused_extreme_magnitudes(scale):
 
 def test_fused_llama_full_size():
     """The LLaMA-shaped decode cache at full size (2,097,152 keys, the
-    benchmark's step): bit for bit the two launches."""
+    benchmark's step, in its launch configuration): bit for bit the two
+    launches, and against the oracle on sampled keys (indices, norms) and
+    sampled tokens (every query head's score, given the GPU's indices)."""
     w = W.llama_decode()
     print("fused vs two launches, LLaMA decode cache", flush=True)
-    _same(w["keys"], w["q"], w["sign_bits"], w["b"], "llama full size")
+    bits, b = w["sign_bits"], w["b"]
+    pf, nf, sf = _same(w["keys"], w["q"], bits, b, "llama full size")
+    d = 128
+    s = A.signs_from_bits(bits)
+    c, t = A.lloyd_max_codebook(d, b)
+    flat = w["keys"].reshape(-1, d)
+    rows = W.sample_rows(flat.shape[0], 8192)
+    y, onorm = A.transform_keys(f64(flat[torch.from_numpy(rows)]), s)
+    gidx = A.unpack_indices(words_u32(pf.reshape(-1, pf.shape[-1]))[rows], d, b)
+    assert_indices(gidx, A.quantize(y, t), y, t, "llama full size, fused")
+    assert_norms(f64(nf.reshape(-1))[rows], onorm, "llama full size, fused")
+    toks = torch.from_numpy(W.sample_rows(pf.shape[2], 1024))
+    tidx = A.unpack_indices(words_u32(pf[:, :, toks]), d, b)
+    tnorm = A.key_norms(f64(w["keys"][:, :, toks]))
+    assert_scores(f64(sf[:, :, toks]), A.transform_queries(f64(w["q"]), s), tidx, tnorm, c,
+                  "llama full size, fused")
 
 
 def test_fused_tiny_workload_oracle():
