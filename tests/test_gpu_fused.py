@@ -65,6 +65,8 @@ SHAPES = [  # (B, Hkv, Hq, T)
     (1, 4, 8, 16),       # G = 2, exactly one unit
     (1, 1, 1, 4096),     # the tiny workload's shape
     (2, 2, 8, 40000),    # several tiles per row
+    (3, 2, 4, 1),        # one token per row
+    (1, 3, 6, 5),        # fewer tokens than a unit
 ]
 
 
