@@ -115,3 +115,26 @@ def test_worst_case_fused_decode(d, b):
         assert dist.max() < 1e-6, label
     worst = assert_scores(f64(scores), qp, gidx, onorm, ADV.codebook(d, b)[0], label)
     assert worst <= ADV.table_rounding_bound(d, b) + FP32_SLACK, (label, worst)
+
+
+@pytest.mark.parametrize("d,b", [(128, 3), (128, 2)])
+def test_worst_case_quantize_score(d, b):
+    """The one-launch write and read path on the same worst case (G = 4, one
+    table per row): its scores against the derived table bound, its records
+    against the oracle's quantization."""
+    m = axr()
+    q, keys, bits = _inputs(d, b, G=4, seed=31)
+    label = f"worst case quantize-and-score d={d} b={b}"
+    print(label, flush=True)
+    packed, norms, scores = m.quantize_score(keys.to(DEV), q.to(DEV), bits, b)
+    torch.cuda.synchronize()
+    ref, cond, qp, gidx, onorm = _oracle_ref(q, keys, packed.cpu(), bits, b)
+    s = A.signs_from_bits(bits)
+    _, t = ADV.codebook(d, b)
+    y, _ = A.transform_keys(f64(keys[0, 0]), s)
+    bad = gidx[0, 0] != A.quantize(y, t)
+    if bad.any():
+        dist = np.min(np.abs(y[bad][:, None] - t[None, :]), axis=1)
+        assert dist.max() < 1e-6, label
+    worst = assert_scores(f64(scores), qp, gidx, onorm, ADV.codebook(d, b)[0], label)
+    assert worst <= ADV.table_rounding_bound(d, b) + FP32_SLACK, (label, worst)
