@@ -148,3 +148,24 @@ def test_fused_tiny_workload_oracle():
     assert_indices(gidx, oidx, y, t, "tiny fused")
     assert_norms(f64(nf), onorm, "tiny fused")
     assert_scores(f64(sf), A.transform_queries(f64(w["q"]), s), gidx, onorm, c, "tiny fused")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fused_random_shapes(seed):
+    """Seeded random shapes (batch, KV heads, group size up to 4, length, b,
+    key and query dtypes) in one launch, bit for bit the two launches."""
+    rng = np.random.default_rng(7300 + seed)
+    B = int(rng.integers(1, 4))
+    Hkv = int(rng.integers(1, 5))
+    G = int(rng.integers(1, 5))
+    T = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 3000)),
+                        int(rng.integers(3000, 20000))]))
+    b = int(rng.choice([2, 3]))
+    kdt = [torch.float32, torch.float16, torch.bfloat16][int(rng.integers(0, 3))]
+    qdt = [torch.float32, torch.float16, torch.bfloat16][int(rng.integers(0, 3))]
+    scale = float(np.exp(rng.uniform(-3.0, 3.0)))
+    keys = torch.from_numpy((rng.standard_normal((B, Hkv, T, 128)) * scale).astype(np.float32))
+    q = torch.from_numpy(rng.standard_normal((B, Hkv * G, 128)).astype(np.float32))
+    label = f"random seed={seed} B={B} Hkv={Hkv} G={G} T={T} b={b} {kdt} {qdt}"
+    print(label, flush=True)
+    _same(keys.to(kdt), q.to(qdt), W.sign_bits(128), b, label)
