@@ -347,9 +347,14 @@ def configs_section(torch, axr, W, stream, reps):
     sr = graph_ms(torch, stream, lambda: axr.score(q, packed.view(1, 1, 4096, 12),
                                                    norms.view(1, 1, 4096), w["sign_bits"], 3,
                                                    out=sc), 16, reps)
+    pk1, nm1 = packed.view(1, 1, 4096, 12), norms.view(1, 1, 4096)
+    fr = graph_ms(torch, stream, lambda: axr.quantize_score(keys, q, w["sign_bits"], 3,
+                                                            packed=pk1, norms=nm1, out=sc),
+                  16, reps)
     out["tiny_d128_b3_n4096"] = {"keys": 4096, "write_us": wr * 1e3, "score_us": sr * 1e3,
+                                 "quantize_score_us": fr * 1e3,
                                  "note": "back to back from a graph; 0.2 MiB per launch, "
-                                         "latency-bound"}
+                                         "latency-bound; quantize_score = both in one launch"}
     log("configs: tiny done")
 
     # LLaMA-3.1-8B decode cache (the headline workload)

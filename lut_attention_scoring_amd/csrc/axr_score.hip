@@ -1064,7 +1064,12 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
   const int64_t target = 256;
   int64_t tiles = (target + rows - 1) / rows;
   int64_t tile_len = (p.T + tiles - 1) / tiles;
-  if (tile_len < 4 * KPB) tile_len = 4 * KPB;   // amortise the table build
+  // amortise the table build over at least four units per wave; with the
+  // keys quantized in the same launch (mode kFused) a unit carries the
+  // write path's work too, and one unit per wave keeps short caches spread
+  // over more CUs
+  const int64_t min_tile = (mode == kFused ? 1 : 4) * KPB;
+  if (tile_len < min_tile) tile_len = min_tile;
   tile_len = (tile_len + KPB - 1) / KPB * KPB;
   tiles = (p.T + tile_len - 1) / tile_len;
   p.tiles = static_cast<int>(tiles);
