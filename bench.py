@@ -419,6 +419,8 @@ def configs_section(torch, axr, W, stream, reps):
         packed, norms = axr.quantize_keys(keys, bits, b)
         lc[f"b{b}"] = {"write": time_write(torch, axr, stream, keys, bits, b, reps),
                        "score": time_score(torch, axr, stream, q, packed, norms, bits, b, reps)}
+        if b == 3:   # G = 8 in one launch (two tables per block)
+            lc["b3"]["quantize_score"] = time_fused(torch, axr, stream, keys, q, bits, b, reps)
         del packed, norms
     out["long_context_t131072_d128"] = dict(keys=keys.numel() // 128, **lc)
     del keys, q

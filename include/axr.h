@@ -195,8 +195,10 @@ int axr_decode_step(const void* q, int q_dtype, const void* k_new, int k_dtype,
  *   packed : device uint32 [B][Hkv][T][W] (output), 16-byte aligned
  *   norms  : device float [B][Hkv][T] (output), 4-byte aligned
  *   scores : device float [B][Hq][T] (output), 4-byte aligned
- * Built for d = 128, b = 2 or 3 and Hq / Hkv <= 4 (one table per (batch, KV
- * head) row); other shapes return AXR_EUNSUPPORTED (use the two calls).
+ * Built for d = 128, b = 2 or 3 with Hq / Hkv <= 4 (one table per (batch, KV
+ * head) row), and for Hq / Hkv = 8 at b = 3 (two tables in one block); each
+ * key is quantized by exactly one block.  Other shapes return
+ * AXR_EUNSUPPORTED (use the two calls).
  * Same further requirements as axr_score, plus T * d * sizeof(key) < 2^31.
  * B = 0 or T = 0 is a no-op.  Errors: AXR_EINVAL, AXR_EUNSUPPORTED,
  * AXR_EALIGN, AXR_EHIP.

@@ -254,7 +254,7 @@ def quantize_score(keys: torch.Tensor, q: torch.Tensor, sign_bits, b: int,
     """Write and read path in one launch: keys [B, Hkv, T, d] and q [B, Hq, d]
     -> (packed int32 [B, Hkv, T, W], norms fp32 [B, Hkv, T], scores fp32
     [B, Hq, T]), the results of quantize_keys followed by score.  Built for
-    d = 128, b = 2 or 3 and Hq / Hkv <= 4."""
+    d = 128, b = 2 or 3 with Hq / Hkv <= 4, and Hq / Hkv = 8 at b = 3."""
     B, Hkv, T, d = keys.shape
     Bq, Hq, dq = q.shape
     if (Bq, dq) != (B, d):

@@ -552,8 +552,12 @@ int axr_quantize_score(const void* keys, int k_dtype, const void* q, int q_dtype
   if (d != 128 || b > 3)
     return fail(AXR_EUNSUPPORTED, "quantize-and-score is built for d=128 and b=2 or 3 (d=%d b=%d)",
                 d, b);
-  if (Hq / Hkv > 4)
-    return fail(AXR_EUNSUPPORTED, "quantize-and-score needs Hq/Hkv <= 4 (got %d)", Hq / Hkv);
+  // every key is quantized by one block: G <= 4 (one table), or G = 8 at
+  // b = 3 (two tables of four heads in one block)
+  const int G = Hq / Hkv;
+  if (G > 4 && !(G == 8 && b == 3))
+    return fail(AXR_EUNSUPPORTED, "quantize-and-score needs Hq/Hkv <= 4, or 8 at b=3 (got %d, b=%d)",
+                G, b);
   // one row of raw keys is addressed with 32-bit offsets
   const int64_t esize = k_dtype == AXR_F32 ? 4 : 2;
   if (T > 0 && T * d * esize > INT32_MAX)

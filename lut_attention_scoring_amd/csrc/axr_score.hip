@@ -31,7 +31,8 @@
 //     that the SIMD's issue arbitration favours take more units and all
 //     waves of the block finish together.  The blocks of a row's head
 //     groups, which read the same records, run on one XCD.
-//   * quantize-and-score (mode kFused, d = 128, b = 2 or 3, one head group):
+//   * quantize-and-score (mode kFused, d = 128, b = 2 or 3, one head group of
+//     up to four heads, or eight at b = 3 with two tables):
 //     each wave loads the raw keys of its unit instead of records, quantizes
 //     them with the write path's lane arithmetic (lane u holds block u,
 //     whose b record words it then looks up), stores records and norms, and
@@ -332,7 +333,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   const int u = lane % S::LPK;                  // 32-coordinate chunk of the key
   const int kw = lane / S::LPK;                 // key index in the wave
   constexpr uint32_t REC_BYTES = S::W * 4;
-  constexpr int CH = 8 / NT < S::NV ? 8 / NT : S::NV;  // steps per batch of lookups
+  // steps per batch of lookups (quantize-and-score with two tables: two,
+  // which keeps its registers near 128; four spilled more and ran 100 µs
+  // against 87 µs on the long-context cache)
+  constexpr int CH = (MODE == kFused && NT == 2) ? 2 : (8 / NT < S::NV ? 8 / NT : S::NV);
   // record units in flight per wave: the 4-coordinate table's units cost
   // the fewest instructions, so more of them are kept in flight (5 measured
   // fastest, against 3, 4, 6 and 8)
@@ -343,8 +347,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(const void* __restrict_
   // coordinates (the write path's layout at d = 128: lane u holds block u
   // and quantizes it into exactly the b record words that it looks up).
   constexpr bool FUSED = MODE == kFused;
-  static_assert(!FUSED || (S::LPK == 4 && NT == 1 && !SG && BITS <= 3),
-                "quantize-and-score is built for d = 128, b = 2 or 3, one head group");
+  static_assert(!FUSED || (S::LPK == 4 && !SG && BITS <= 3),
+                "quantize-and-score is built for d = 128, b = 2 or 3");
   constexpr int KW = FUSED ? RawWords<KDT>::kWords : 4;   // raw words per lane
   constexpr uint32_t KEY_BYTES = D * (KDT == AXR_F32 ? 4u : 2u);
   // tokens [0, len) of this batch row are scored: T, or lens[bi] (clamped),
@@ -1086,7 +1090,9 @@ int launch_nt(const void* q, int qdt, const uint32_t* packed, const float* norms
   }
   const dim3 g(static_cast<unsigned>(grid)), blk(NTHREADS);
   if (mode == kFused) {
-    if constexpr (S::LPK == 4 && NT == 1 && !SG && BITS <= 3) {
+    // every key is quantized by exactly one block: one head group per row
+    if (p.head_groups != 1) return static_cast<int>(hipErrorInvalidValue);
+    if constexpr (S::LPK == 4 && !SG && BITS <= 3) {
       switch (p.kdt) {
         case AXR_F32:
           hipLaunchKernelGGL((score_kernel<D, BITS, P, NT, NTHREADS, kFused, SG, AXR_F32>), g,

@@ -130,7 +130,9 @@ def test_quantize_score_validation():
     # shapes the one-launch path is not built for are rejected, not routed
     assert _qs(d=256)[0] == axr.EUNSUPPORTED
     assert _qs(b=4)[0] == axr.EUNSUPPORTED
-    assert _qs(Hq=16, Hkv=2)[0] == axr.EUNSUPPORTED
+    assert _qs(Hq=16, Hkv=2, b=2)[0] == axr.EUNSUPPORTED   # G = 8 only at b = 3
+    assert _qs(Hq=12, Hkv=2)[0] == axr.EUNSUPPORTED        # G = 6: two head groups
+    assert _qs(Hq=32, Hkv=2)[0] == axr.EUNSUPPORTED        # G = 16
     assert _qs(kdt=7)[0] == axr.EUNSUPPORTED
     assert _qs(qdt=7)[0] == axr.EUNSUPPORTED
     assert _qs(T=(1 << 23) + 1)[0] == axr.EUNSUPPORTED     # > 2 GiB of fp16 keys per row

@@ -81,6 +81,57 @@ def test_fused_matches_two_launches(shape, b, dtype):
     _same(keys, q, W.sign_bits(128), b, f"{shape} b={b} {dtype}")
 
 
+SHAPES_G8 = [  # (B, Hkv, Hq, T): eight query heads per KV head, two tables per block
+    (2, 2, 16, 1000),    # ragged tail
+    (1, 1, 8, 17),       # one full unit and one key
+    (1, 2, 16, 40000),   # several tiles per row
+    (2, 1, 8, 1),        # one token per row
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("shape", SHAPES_G8)
+def test_fused_g8_matches_two_launches(shape, dtype):
+    B, Hkv, Hq, T = shape
+    rng = np.random.default_rng(7400 + 97 * T + 13 * Hq)
+    keys, q = _inputs(rng, B, Hkv, Hq, T, dtype)
+    print(f"fused vs two launches, G = 8 {shape} {dtype}", flush=True)
+    _same(keys, q, W.sign_bits(128), 3, f"G=8 {shape} {dtype}")
+
+
+def test_fused_g8_against_oracle():
+    B, Hkv, Hq, T = 1, 2, 16, 700
+    rng = np.random.default_rng(7500)
+    keys, q = _inputs(rng, B, Hkv, Hq, T, torch.bfloat16)
+    bits = W.sign_bits(128)
+    pf, nf, sf = _same(keys, q, bits, 3, "oracle G=8")
+    s = A.signs_from_bits(bits)
+    c, t = A.lloyd_max_codebook(128, 3)
+    y, onorm = A.transform_keys(f64(keys), s)
+    gidx = A.unpack_indices(words_u32(pf), 128, 3)
+    assert_indices(gidx, A.quantize(y, t), y, t, "fused G=8")
+    assert_norms(f64(nf), onorm, "fused G=8")
+    assert_scores(f64(sf), A.transform_queries(f64(q), s), gidx, onorm, c, "fused G=8")
+
+
+def test_fused_long_context_full_size():
+    """The long-context cache at full size (1,048,576 bf16 keys, G = 8, b = 3):
+    bit for bit the two launches, and sampled tokens against the oracle."""
+    w = W.long_context(b=3)
+    print("fused vs two launches, long-context cache", flush=True)
+    bits, b, d = w["sign_bits"], w["b"], 128
+    pf, nf, sf = _same(w["keys"], w["q"], bits, b, "long context full size")
+    s = A.signs_from_bits(bits)
+    c, t = A.lloyd_max_codebook(d, b)
+    toks = torch.from_numpy(W.sample_rows(pf.shape[2], 1024))
+    y, onorm = A.transform_keys(f64(w["keys"][:, :, toks]).reshape(-1, d), s)
+    tidx = A.unpack_indices(words_u32(pf[:, :, toks]), d, b)
+    assert_indices(tidx.reshape(-1, d), A.quantize(y, t), y, t, "long context, fused")
+    tnorm = A.key_norms(f64(w["keys"][:, :, toks]))
+    assert_scores(f64(sf[:, :, toks]), A.transform_queries(f64(w["q"]), s), tidx, tnorm, c,
+                  "long context, fused")
+
+
 @pytest.mark.parametrize("b", [2, 3])
 def test_fused_against_oracle(b):
     B, Hkv, Hq, T = 2, 2, 8, 700
